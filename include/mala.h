@@ -1,0 +1,173 @@
+/*
+ * mala.h - C ABI of the MassAlloc Attention (MALA) operator library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * MALA ("MassAlloc Attention: Let Attention Allocate Its Own Compute",
+ * arXiv HTML 2609.32712) is causal softmax attention that scores every legal
+ * Q.K tile but runs the post-score work of a tile only when some valid query
+ * row's normalised contribution reaches tau / L_q (Sec. 2.1; L_q = number of
+ * keys the query sees). Forward tests against the running online-softmax
+ * state (Sec. 2.2, Eqs. 1-3; Appendix A, Algorithm 1); backward tests against
+ * the final log-normaliser saved by forward (Sec. 2.2, Eq. 4; Algorithm 2);
+ * split-KV decode applies the forward rule per split and merges the partial
+ * (m, l, u) (Sec. 2.4; Appendix A.1). A dense FullAttn path built from the
+ * same kernels, with the test compiled out, serves as the comparison.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *     keeps no state between calls, allocates no memory, never synchronises
+ *     the device, and enqueues all work on `stream` (a hipStream_t; NULL is
+ *     the default stream).
+ *   - Layouts are contiguous row-major:
+ *       Q, O, dO, dQ   [batch][heads_q ][seqlen_q][head_dim]  bf16
+ *       K, V, dK, dV   [batch][heads_kv][seqlen_k][head_dim]  bf16
+ *       LSE            [batch][heads_q ][seqlen_q]            fp32
+ *     LSE holds z_q = log Z_R,q, the natural log of the retained normaliser
+ *     of the scaled scores (Sec. 2.2, end of "Online Sparse Softmax").
+ *   - Query head h reads KV head h / (heads_q / heads_kv) (grouped-query
+ *     attention; heads_q must be a multiple of heads_kv).
+ *   - head_dim is 64 or 128. The decision tile is block_q x block_k; this
+ *     build supports 64 x 64. Forward and backward must use the same tile
+ *     (the nesting of Sec. 2.2 relies on one partition).
+ *   - Scores are s = softmax_scale * <q, k> (the paper folds the scale into
+ *     Q, Sec. 2.1); pass 1/sqrt(head_dim) for standard attention.
+ *   - Every argument is validated before any device call. On an invalid
+ *     argument nothing is enqueued and a mala_status code is returned;
+ *     mala_status_string() gives its text. Nothing throws across the ABI.
+ */
+#ifndef MALA_H_
+#define MALA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MALA_OK = 0,
+  MALA_ERR_INVALID_ARG = 1, /* null pointer, bad size, bad tau/scale, ... */
+  MALA_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim, tile size */
+  MALA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+  MALA_ERR_DEVICE = 4,      /* no usable HIP device / wrong architecture */
+  MALA_ERR_LAUNCH = 5       /* a kernel launch failed */
+} mala_status;
+
+typedef struct {
+  int32_t batch;     /* >= 1 */
+  int32_t heads_q;   /* >= 1, multiple of heads_kv */
+  int32_t heads_kv;  /* >= 1 */
+  int32_t seqlen_q;  /* >= 1 (1 for decode) */
+  int32_t seqlen_k;  /* >= 1 */
+  int32_t head_dim;  /* 64 or 128 */
+} mala_shape;
+
+typedef struct {
+  /* 1: causal with L_q = q + 1 (zero-based), requires seqlen_q == seqlen_k
+   *    (equal-length causal training, Sec. 2.1);
+   * 0: every query sees all seqlen_k keys, L_q = seqlen_k. Ignored by
+   *    decode, which always uses L = seqlen_k (Sec. 2.1, decoding). */
+  int32_t causal;
+  int32_t block_q;     /* decision tile rows; 64 */
+  int32_t block_k;     /* decision tile keys; 64 */
+  float tau;           /* tolerance, >= 0; 0 never skips (Sec. 2.3: tau -> 0
+                          recovers FullAttn); +inf allowed; NaN / < 0
+                          rejected. Ignored by the fullattn_* entry points. */
+  float softmax_scale; /* > 0 and finite */
+} mala_config;
+
+/* Optional instrumentation for tests and measurement; pass NULL in timed
+ * and production calls. With it NULL the operator writes only its outputs.
+ *   counters  device uint64[4], accumulated (not cleared) by the call:
+ *             [0] legal tiles tested, [1] retained tiles,
+ *             [2] retained post-score key slots (valid rows x block_k per
+ *                 retained tile: the count of Sec. 2.3 / Eq. 11),
+ *             [3] V tiles loaded from HBM (forward and decode).
+ *   decisions device uint8, one byte per tile, written 1 (retained) or
+ *             0 (skipped) for every legal tile the call tests; other bytes
+ *             are left untouched. Layout [batch][heads_q][Tr][Tc] for
+ *             forward and backward (Tr = ceil(seqlen_q/block_q),
+ *             Tc = ceil(seqlen_k/block_k)), [batch][heads_q][Tc] for decode.
+ * Either member may be NULL. */
+typedef struct {
+  unsigned long long* counters;
+  uint8_t* decisions;
+} mala_stats;
+
+/* MALA forward (Algorithm 1; Eqs. 1-3; Appendix A.1 "Fused forward
+ * execution"). Per (batch, query head, query block), key blocks holding a
+ * legal key are visited from the last one (the diagonal when causal) down to
+ * block 0. Each tile is scored; it is skipped when every valid query row with
+ * a legal key in it has rowmax - m - log l < log(tau / L_q); otherwise V is
+ * loaded and every valid row of the block takes the online-softmax update.
+ * Writes O (bf16) and LSE (fp32) only. Works for training and prefill. */
+int mala_fwd(const mala_shape* shape, const mala_config* cfg, const void* q, const void* k,
+             const void* v, void* o, float* lse, const mala_stats* stats, void* stream);
+
+/* Dense FullAttn forward from the same kernel with the test compiled out
+ * (every legal tile retained). cfg->tau is ignored. */
+int fullattn_fwd(const mala_shape* shape, const mala_config* cfg, const void* q, const void* k,
+                 const void* v, void* o, float* lse, const mala_stats* stats, void* stream);
+
+/* Bytes of device workspace mala_bwd / fullattn_bwd need (fp32 row terms
+ * D = rowsum(O o dO) and an fp32 dQ accumulator). Returns 0 for an invalid
+ * shape or config. */
+size_t mala_bwd_workspace_bytes(const mala_shape* shape, const mala_config* cfg);
+
+/* MALA backward (Algorithm 2; Eq. 4; Appendix A.1 "Fused backward
+ * execution"). Key-major: per (batch, KV head, key block), query blocks are
+ * visited for every query head of the group. Q.K is recomputed; a tile is
+ * skipped when every legal entry has s - z_q < log(tau / L_q), with z = the
+ * forward's LSE; otherwise P = exp(s - z), dP = dO V^T,
+ * dS = P o (dP - rowsum(O o dO)) and the dV, dK, dQ products run. o and lse
+ * are the forward's outputs. dQ, dK, dV are overwritten. workspace must hold
+ * mala_bwd_workspace_bytes(); its contents on entry are irrelevant. */
+int mala_bwd(const mala_shape* shape, const mala_config* cfg, const void* q, const void* k,
+             const void* v, const void* o, const float* lse, const void* dout, void* dq,
+             void* dk, void* dv, void* workspace, size_t workspace_bytes,
+             const mala_stats* stats, void* stream);
+
+/* Dense FullAttn backward from the same kernel, test compiled out. */
+int fullattn_bwd(const mala_shape* shape, const mala_config* cfg, const void* q, const void* k,
+                 const void* v, const void* o, const float* lse, const void* dout, void* dq,
+                 void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                 const mala_stats* stats, void* stream);
+
+/* Bytes of device workspace for split-KV decode with num_splits splits
+ * (fp32 partial m, l and u per split and query head). 0 if invalid. */
+size_t mala_decode_workspace_bytes(const mala_shape* shape, int32_t num_splits);
+
+/* A split count that fills the GPU for this shape (advisory; decisions
+ * depend on the split count, so callers comparing runs must fix it). */
+int32_t mala_decode_default_splits(const mala_shape* shape);
+
+/* Split-KV MALA decode (Sec. 2.4; Appendix A.1 "Fused decoding execution").
+ * One new query per sequence: q, o are [batch][heads_q][head_dim], lse is
+ * [batch][heads_q]; k_cache, v_cache are [batch][heads_kv][seqlen_k][head_dim]
+ * and include the current token (L = seqlen_k, Sec. 2.1). shape->seqlen_q
+ * must be 1. The Tc = ceil(seqlen_k/block_k) key tiles are cut into
+ * num_splits ranges of ceil(Tc/num_splits) tiles; each range starts with
+ * fresh (m, l), visits its tiles last-to-first and tests each head's row
+ * against its own partial normaliser; the partial (m, l, u) are merged with
+ * the normaliser-aware reduction. Every cached key is scored; a V tile is
+ * read only if some query head of the KV group retains it. */
+int mala_decode(const mala_shape* shape, const mala_config* cfg, const void* q,
+                const void* k_cache, const void* v_cache, void* o, float* lse,
+                int32_t num_splits, void* workspace, size_t workspace_bytes,
+                const mala_stats* stats, void* stream);
+
+/* Dense split-KV decode from the same kernels, test compiled out. */
+int fullattn_decode(const mala_shape* shape, const mala_config* cfg, const void* q,
+                    const void* k_cache, const void* v_cache, void* o, float* lse,
+                    int32_t num_splits, void* workspace, size_t workspace_bytes,
+                    const mala_stats* stats, void* stream);
+
+/* Static text for a status code (never NULL). */
+const char* mala_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MALA_H_ */

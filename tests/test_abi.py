@@ -1,0 +1,150 @@
+"""CPU tests of the C ABI: the library loads, exports every function that
+include/mala.h declares, and every validation error path returns its status
+before any device call. No compute call is made: each call below carries at
+least one invalid argument, except the no-device check, which only runs
+where no GPU is visible."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import adaptive_softmax_attention_amd as m
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mala.h")
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:mala|fullattn)_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    L = m.lib()
+    names = declared_functions()
+    assert len(names) == 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(m.EXPORTS)
+
+
+def test_status_strings():
+    for code in range(6):
+        s = m.mala_status_string(code)
+        assert isinstance(s, str) and s
+    assert m.mala_status_string(99) == "unknown status"
+
+
+def shape(B=1, Hq=4, Hkv=2, Nq=128, Nk=128, d=128):
+    return m.Shape(B, Hq, Hkv, Nq, Nk, d)
+
+
+def cfg(causal=1, bq=64, bk=64, tau=1.0, scale=None):
+    return m.Config(causal, bq, bk, tau, 0.088 if scale is None else scale)
+
+
+def fwd(s, c, q=FAKE, fn="mala_fwd"):
+    return getattr(m.lib(), fn)(ctypes.byref(s) if s is not None else None,
+                                ctypes.byref(c) if c is not None else None,
+                                q, FAKE, FAKE, FAKE, FAKE, None, None)
+
+
+@pytest.mark.parametrize("s,c,expect", [
+    (None, cfg(), m.MALA_ERR_INVALID_ARG),
+    (shape(), None, m.MALA_ERR_INVALID_ARG),
+    (shape(B=0), cfg(), m.MALA_ERR_INVALID_ARG),
+    (shape(Hq=3, Hkv=2), cfg(), m.MALA_ERR_INVALID_ARG),
+    (shape(Nq=0, Nk=0), cfg(), m.MALA_ERR_INVALID_ARG),
+    (shape(d=96), cfg(), m.MALA_ERR_UNSUPPORTED),
+    (shape(d=0), cfg(), m.MALA_ERR_INVALID_ARG),
+    (shape(), cfg(bq=128, bk=128), m.MALA_ERR_UNSUPPORTED),
+    (shape(), cfg(bq=0), m.MALA_ERR_INVALID_ARG),
+    (shape(), cfg(tau=float("nan")), m.MALA_ERR_INVALID_ARG),
+    (shape(), cfg(tau=-1.0), m.MALA_ERR_INVALID_ARG),
+    (shape(), cfg(scale=0.0), m.MALA_ERR_INVALID_ARG),
+    (shape(), cfg(scale=float("inf")), m.MALA_ERR_INVALID_ARG),
+    (shape(), cfg(scale=float("nan")), m.MALA_ERR_INVALID_ARG),
+    (shape(), cfg(causal=2), m.MALA_ERR_INVALID_ARG),
+    (shape(Nq=100, Nk=128), cfg(causal=1), m.MALA_ERR_UNSUPPORTED),
+    (shape(Nq=1 << 25, Nk=1 << 25), cfg(), m.MALA_ERR_UNSUPPORTED),
+])
+def test_forward_validation(s, c, expect):
+    assert fwd(s, c) == expect
+
+
+def test_forward_null_pointer():
+    assert fwd(shape(), cfg(), q=None) == m.MALA_ERR_INVALID_ARG
+
+
+def test_fullattn_ignores_tau_but_checks_the_rest():
+    # tau NaN is not an error for the dense path; a bad scale still is
+    assert fwd(shape(), cfg(scale=-1.0), fn="fullattn_fwd") == m.MALA_ERR_INVALID_ARG
+    rc = fwd(shape(B=0), cfg(tau=float("nan")), fn="fullattn_fwd")
+    assert rc == m.MALA_ERR_INVALID_ARG
+
+
+def _no_gpu():
+    try:
+        import torch
+        return torch.cuda.device_count() == 0
+    except Exception:
+        return True
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="only meaningful where no GPU is visible")
+def test_valid_call_without_device_reports_device_error():
+    assert fwd(shape(), cfg()) == m.MALA_ERR_DEVICE
+    assert fwd(shape(), cfg(tau=float("nan")), fn="fullattn_fwd") == m.MALA_ERR_DEVICE
+
+
+def test_workspace_sizes():
+    L = m.lib()
+    s, c = shape(B=2, Hq=4, Nq=100, Nk=100, d=64), cfg()
+    rows = 2 * 4 * 100
+    a256 = lambda x: (x + 255) // 256 * 256
+    assert L.mala_bwd_workspace_bytes(ctypes.byref(s), ctypes.byref(c)) == a256(rows * 4) + a256(rows * 64 * 4)
+    assert L.mala_bwd_workspace_bytes(ctypes.byref(shape(d=96)), ctypes.byref(c)) == 0
+    sd = shape(B=3, Hq=8, Hkv=2, Nq=1, Nk=1000, d=128)
+    n = 3 * 8 * 5
+    assert L.mala_decode_workspace_bytes(ctypes.byref(sd), 5) == 2 * a256(n * 4) + a256(n * 128 * 4)
+    assert L.mala_decode_workspace_bytes(ctypes.byref(sd), 0) == 0
+    assert 1 <= L.mala_decode_default_splits(ctypes.byref(sd)) <= 16
+
+
+def bwd(s, c, ws=FAKE, nbytes=1 << 40, dq=FAKE):
+    return m.lib().mala_bwd(ctypes.byref(s), ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                            dq, FAKE, FAKE, ws, nbytes, None, None)
+
+
+def test_backward_validation():
+    assert bwd(shape(), cfg(), ws=None) == m.MALA_ERR_WORKSPACE
+    assert bwd(shape(), cfg(), nbytes=16) == m.MALA_ERR_WORKSPACE
+    assert bwd(shape(), cfg(), dq=None) == m.MALA_ERR_INVALID_ARG
+    assert bwd(shape(Nq=64, Nk=128), cfg()) == m.MALA_ERR_UNSUPPORTED
+    assert bwd(shape(), cfg(tau=-2.0)) == m.MALA_ERR_INVALID_ARG
+
+
+def dec(s, c, S=4, ws=FAKE, nbytes=1 << 40):
+    return m.lib().mala_decode(ctypes.byref(s), ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, S,
+                               ws, nbytes, None, None)
+
+
+def test_decode_validation():
+    s = shape(Nq=1, Nk=4096)
+    assert dec(shape(Nq=2, Nk=4096), cfg()) == m.MALA_ERR_INVALID_ARG
+    assert dec(s, cfg(), S=0) == m.MALA_ERR_INVALID_ARG
+    assert dec(s, cfg(), S=65) == m.MALA_ERR_INVALID_ARG  # more splits than tiles
+    assert dec(s, cfg(), ws=None) == m.MALA_ERR_WORKSPACE
+    assert dec(s, cfg(), nbytes=100) == m.MALA_ERR_WORKSPACE
+    assert dec(s, cfg(tau=float("nan"))) == m.MALA_ERR_INVALID_ARG
+
+
+def test_binding_rejects_bad_tensors():
+    import torch
+    q = torch.zeros(1, 2, 64, 64, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        m.mala_fwd(q, q, q, q, q[..., 0])
