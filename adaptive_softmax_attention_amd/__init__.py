@@ -78,6 +78,10 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: run __graft_entry__.build() "
                               "(or python -m adaptive_softmax_attention_amd.build)")
+        # torch ships its own HIP runtime under the same soname; loading it
+        # first makes the library bind to that one instance instead of
+        # pulling a second runtime into the process
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         P, vp, sz = ctypes.POINTER, ctypes.c_void_p, ctypes.c_size_t
         ps, pc, pst = P(Shape), P(Config), P(_CStats)
