@@ -153,6 +153,7 @@ int decode_common(const mala_shape* shape, const mala_config* cfg, const void* q
   if (st) return st;
   if (shape->seqlen_q != 1) return MALA_ERR_INVALID_ARG;
   if (!q || !k_cache || !v_cache || !o || !lse) return MALA_ERR_INVALID_ARG;
+  if (shape->heads_q / shape->heads_kv > 8) return MALA_ERR_UNSUPPORTED;
   if (num_splits < 1) return MALA_ERR_INVALID_ARG;
   const int64_t tc = (shape->seqlen_k + 63) / 64;
   if (num_splits > tc) return MALA_ERR_INVALID_ARG;  // every split owns >= 1 tile

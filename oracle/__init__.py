@@ -42,7 +42,7 @@ ROUND_OUT = 8
 EXACT = 0
 BF16_FWD = ROUND_P_FWD | ROUND_OUT
 BF16_BWD = ROUND_P_BWD | ROUND_DS | ROUND_OUT
-BF16_DECODE = ROUND_P_FWD | ROUND_OUT
+BF16_DECODE = ROUND_OUT  # the decode kernel forms P V in fp32
 
 ILLEGAL, SKIP, RETAIN = -1, 0, 1
 

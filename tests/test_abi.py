@@ -141,6 +141,7 @@ def test_decode_validation():
     assert dec(s, cfg(), ws=None) == m.MALA_ERR_WORKSPACE
     assert dec(s, cfg(), nbytes=100) == m.MALA_ERR_WORKSPACE
     assert dec(s, cfg(tau=float("nan"))) == m.MALA_ERR_INVALID_ARG
+    assert dec(shape(Hq=16, Hkv=1, Nq=1, Nk=4096), cfg()) == m.MALA_ERR_UNSUPPORTED
 
 
 def test_binding_rejects_bad_tensors():
