@@ -39,6 +39,8 @@ ROUND_P_FWD = 1
 ROUND_P_BWD = 2
 ROUND_DS = 4
 ROUND_OUT = 8
+ABS = 16  # magnitude mode: sums of |a|*|b| instead of a*b (error-bound scale)
+ABS_D = 32  # backward: dS -> P * sum_d |O||dO| in dQ / dK (sensitivity to D)
 EXACT = 0
 BF16_FWD = ROUND_P_FWD | ROUND_OUT
 BF16_BWD = ROUND_P_BWD | ROUND_DS | ROUND_OUT

@@ -48,6 +48,13 @@
 #define ORC_ROUND_P_BWD 2  /* P before the dV product */
 #define ORC_ROUND_DS 4     /* dS before the dK and dQ products */
 #define ORC_ROUND_OUT 8    /* O, dQ, dK, dV stored as bf16; LSE as fp32 */
+#define ORC_ABS 16         /* magnitude mode: every product term a*b is replaced
+                              by |a|*|b| (P >= 0 stays P), giving per output
+                              element the sum of absolute terms that rounding
+                              error bounds scale with */
+#define ORC_ABS_D 32       /* backward sensitivity to D: dS replaced by
+                              P * sum_d |O||dO| in the dQ / dK sums (|K|, |Q|
+                              operands), dV gets no term (it has no D) */
 
 typedef struct {
   int32_t batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim;
@@ -298,7 +305,10 @@ static void online_block(const orc_problem* p, const double* q, int64_t q_stride
         rowsum += pt;
         const double pu = (p->round_flags & ORC_ROUND_P_FWD) ? round_bf16(pt) : pt;
         const double* vv = vbase + (k0 + c) * d;
-        for (int e = 0; e < d; ++e) acc[r * d + e] += pu * vv[e];
+        if (p->round_flags & ORC_ABS)
+          for (int e = 0; e < d; ++e) acc[r * d + e] += pu * fabs(vv[e]);
+        else
+          for (int e = 0; e < d; ++e) acc[r * d + e] += pu * vv[e];
       }
       l[r] = alpha * l[r] + rowsum;
       m[r] = m_new;
@@ -393,8 +403,8 @@ static double bwd_tile_margin(const orc_problem* p, const double* q, const doubl
  * the pointers address the first row of the tile's query / key block. */
 static void bwd_tile_apply(const orc_problem* p, const double* q, const double* k,
                            const double* v, const double* lse, const double* dout,
-                           const double* D, int64_t b, int64_t h, int64_t i, int64_t j,
-                           double* dq_rows, double* dk_rows, double* dv_rows) {
+                           const double* D, const double* Dabs, int64_t b, int64_t h, int64_t i,
+                           int64_t j, double* dq_rows, double* dk_rows, double* dv_rows) {
   const int d = p->head_dim, G = p->heads_q / p->heads_kv;
   const int64_t Nq = p->seqlen_q, Nk = p->seqlen_k, g = h / G;
   for (int64_t qi = i * p->block_q; qi < (i + 1) * p->block_q && qi < Nq; ++qi) {
@@ -407,16 +417,19 @@ static void bwd_tile_apply(const orc_problem* p, const double* q, const double* 
       const double dp = dot(dout + row * d, v + krow * d, d);  /* Alg. 2 step 13 */
       const double ds = pr * (dp - D[row]);                    /* Alg. 2 step 14 */
       const double pu = (p->round_flags & ORC_ROUND_P_BWD) ? round_bf16(pr) : pr;
-      const double du = (p->round_flags & ORC_ROUND_DS) ? round_bf16(ds) : ds;
+      double du = (p->round_flags & ORC_ROUND_DS) ? round_bf16(ds) : ds;
+      const int dsens = (p->round_flags & ORC_ABS_D) != 0;
+      const int mag = (p->round_flags & ORC_ABS) != 0 || dsens;
+      if (mag) du = dsens ? pr * Dabs[row] : fabs(du);
       if (dq_rows) {
         double* dqr = dq_rows + (qi - i * p->block_q) * d;
-        for (int c = 0; c < d; ++c) dqr[c] += du * k[krow * d + c];
+        for (int c = 0; c < d; ++c) dqr[c] += du * (mag ? fabs(k[krow * d + c]) : k[krow * d + c]);
       } else {
         double* dkr = dk_rows + (kj - j * p->block_k) * d;
         double* dvr = dv_rows + (kj - j * p->block_k) * d;
         for (int c = 0; c < d; ++c) {
-          dkr[c] += du * q[row * d + c];
-          dvr[c] += pu * dout[row * d + c];
+          dkr[c] += du * (mag ? fabs(q[row * d + c]) : q[row * d + c]);
+          if (!dsens) dvr[c] += pu * (mag ? fabs(dout[row * d + c]) : dout[row * d + c]);
         }
       }
     }
@@ -443,7 +456,13 @@ int orc_mala_bwd(const orc_problem* p, const double* q, const double* k, const d
   /* D_q = rowsum(O o dO) from the stored O (Alg. 2 step 14) */
   const int64_t nrow = (int64_t)p->batch * p->heads_q * Nq;
   double* D = (double*)malloc(sizeof(double) * (size_t)(nrow > 0 ? nrow : 1));
-  for (int64_t r = 0; r < nrow; ++r) D[r] = dot(o + r * d, dout + r * d, d);
+  double* Dabs = (double*)malloc(sizeof(double) * (size_t)(nrow > 0 ? nrow : 1));
+  for (int64_t r = 0; r < nrow; ++r) {
+    D[r] = dot(o + r * d, dout + r * d, d);
+    double a = 0.0;
+    for (int c = 0; c < d; ++c) a += fabs(o[r * d + c] * dout[r * d + c]);
+    Dabs[r] = a;
+  }
 
   /* decisions for every tile the selected blocks touch */
   int8_t* dd = dec ? dec : (int8_t*)malloc((size_t)(ntiles > 0 ? ntiles : 1));
@@ -494,7 +513,7 @@ int orc_mala_bwd(const orc_problem* p, const double* q, const double* k, const d
     for (int64_t j = 0; j < Tc; ++j) {
       const int64_t ti = ((b * p->heads_q + h) * Tr + i) * Tc + j;
       if (dd[ti] == ORC_RETAIN)
-        bwd_tile_apply(p, q, k, v, lse, dout, D, b, h, i, j, rows, NULL, NULL);
+        bwd_tile_apply(p, q, k, v, lse, dout, D, Dabs, b, h, i, j, rows, NULL, NULL);
     }
     for (int64_t x = 0; x < (q1 - q0) * d; ++x) {
       rows[x] *= p->scale;
@@ -516,7 +535,7 @@ int orc_mala_bwd(const orc_problem* p, const double* q, const double* k, const d
       for (int64_t i = 0; i < Tr; ++i) {
         const int64_t ti = ((b * p->heads_q + h) * Tr + i) * Tc + j;
         if (dd[ti] == ORC_RETAIN)
-          bwd_tile_apply(p, q, k, v, lse, dout, D, b, h, i, j, NULL, krows, vrows);
+          bwd_tile_apply(p, q, k, v, lse, dout, D, Dabs, b, h, i, j, NULL, krows, vrows);
       }
     for (int64_t x = 0; x < (k1 - k0) * d; ++x) {
       krows[x] *= p->scale;
@@ -528,6 +547,7 @@ int orc_mala_bwd(const orc_problem* p, const double* q, const double* k, const d
   }
   if (!dec) free(dd);
   free(D);
+  free(Dabs);
   return 0;
 }
 

@@ -1,11 +1,23 @@
 """GPU-versus-oracle comparison helpers (test code).
 
-Tolerances (per tensor X in {O, dQ, dK, dV}, stated once here):
-  * V1: |X_gpu - X_exact| <= 2e-2 * max(1, |X_exact|) elementwise against the
-    fp64 oracle;
-  * V2: sum|X_gpu - X_bf16| / sum|X_bf16| <= 1e-3 against the oracle's
-    bf16-operand model (P~, P and dS rounded to bf16 before the products,
-    outputs rounded to bf16);
+Tolerances (per tensor X in {O, dQ, dK, dV}, stated once here). X_bf16 is
+the oracle's bf16-operand model: fp64 arithmetic with P~, P and dS rounded to
+bf16 where the kernels feed them to bf16 products, outputs rounded to bf16.
+M is the oracle's magnitude of each element (the same sum with every term
+replaced by |a|*|b|).
+  * V1 (elementwise, derived from the arithmetic): the kernels and the model
+    differ only where fp32 (kernel) and fp64 (model) intermediates round to
+    different bf16 neighbours, each such flip moving one operand by at most
+    2^-7 of itself, plus fp32 accumulation error; hence
+    |X_gpu - X_bf16| <= 2^-7 (M + |X_bf16| + M_D) + 1e-4, where M_D (backward
+    dQ, dK only) covers flips of the stored O inside D = rowsum(O o dO): each
+    moves D_q by at most 2^-7 sum_d |O_qd dO_qd| and dS by P times that, so
+    M_D is the dQ / dK sum with dS replaced by P * sum_d |O dO|;
+  * V2: sum|X_gpu - X_bf16| / sum|X_bf16| <= 1e-3 (mean relative error);
+  * L2 (fidelity to the fp64 oracle, the relative L2 error the paper uses,
+    App. C.3): ||X_gpu - X_exact|| / ||X_exact|| <= 2^-7 (||M|| / ||X_exact|| + 1)
+    (bf16 operand rounding, at most 2^-9 of each term, with a factor 4 of
+    headroom for the rounding of the intermediates themselves);
   * LSE: |delta| <= 1e-3 (nats);
   * decisions: agreement >= 99.9% of legal tiles, and a tile may differ only
     where the oracle's margin is within DELTA = 2e-3 nats of zero. Such a
@@ -41,10 +53,19 @@ def gpu_to_f64(t):
     return t.float().cpu().numpy().astype(np.float64)
 
 
-def v1_ok(x, ref):
-    err = np.abs(x - ref)
-    bound = V1_TOL * np.maximum(1.0, np.abs(ref))
+def v1_ok(x, model, mag, mag_d=0.0):
+    err = np.abs(x - model)
+    bound = 2.0 ** -7 * (mag + np.abs(model) + mag_d) + 1e-4
     return bool((err <= bound).all()), float((err / bound).max()) if err.size else 0.0
+
+
+def l2_ok(x, exact, mag):
+    ne = np.linalg.norm(exact)
+    if ne == 0:
+        return bool(np.linalg.norm(x) == 0), 0.0
+    rel = float(np.linalg.norm(x - exact) / ne)
+    bound = 2.0 ** -7 * (np.linalg.norm(mag) / ne + 1.0)
+    return rel <= bound, rel
 
 
 def v2(x, ref_bf):
@@ -83,6 +104,17 @@ def settle_fwd_branch(run_oracle, gpu_dec, legal_mask, free=None, max_iter=16):
 
 
 def check_decisions(gpu_dec, ora, legal):
+    """Every GPU decision that differs from the oracle's must sit within
+    DELTA of the threshold; with >= 1000 legal tiles the agreement rate must
+    also reach AGREE_MIN (tiny problems can be dominated by exact ties, e.g.
+    row 0 at tau = 1, where P = 1 = tau / L). Returns the agreement rate."""
     n = int(legal.sum())
-    agree = int((legal & (gpu_dec == ora["dec"])).sum())
-    return agree / max(1, n)
+    dis = legal & (gpu_dec != ora["dec"])
+    if dis.any():
+        mg = ora["margin"][dis]
+        assert np.all(np.isfinite(mg) & (np.abs(mg) < DELTA)), (
+            f"{int(dis.sum())} decisions differ; oracle margins {mg[:8]}")
+    agree = 1.0 - int(dis.sum()) / max(1, n)
+    if n >= 1000:
+        assert agree >= AGREE_MIN, agree
+    return agree

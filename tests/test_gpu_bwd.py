@@ -1,0 +1,216 @@
+"""GPU parity of the backward entry points (mala_bwd, fullattn_bwd) against
+the CPU oracle, through the C ABI. The oracle backward consumes the oracle's
+own forward outputs (O rounded to bf16 and LSE to fp32 in the bf16-operand
+model), never the GPU's. Tolerances: tests/parity.py."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from parity import (AGREE_MIN, DELTA, LSE_TOL, V2_TOL, bits_to_f64, bits_to_gpu,
+                    check_decisions, gpu_to_f64, l2_ok, settle_fwd_branch, v1_ok, v2)
+
+pytestmark = pytest.mark.gpu
+
+
+def mala():
+    import adaptive_softmax_attention_amd as m
+    m.lib()
+    return m
+
+
+def run_fwd_bwd(inp, tau, causal=True, dense=False):
+    m = mala()
+    q, k, v, do = (bits_to_gpu(inp[x]) for x in ("q", "k", "v", "do"))
+    B, Hq, Nq, d = q.shape
+    Nk = k.shape[2]
+    Tr, Tc = -(-Nq // 64), -(-Nk // 64)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device="cuda")
+    fst = m.Stats(torch.zeros(4, dtype=torch.int64, device="cuda"),
+                  torch.full((B, Hq, Tr, Tc), 255, dtype=torch.uint8, device="cuda"))
+    bst = m.Stats(torch.zeros(4, dtype=torch.int64, device="cuda"),
+                  torch.full((B, Hq, Tr, Tc), 255, dtype=torch.uint8, device="cuda"))
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(m.mala_bwd_workspace_bytes(q, k, causal=causal), dtype=torch.uint8,
+                     device="cuda")
+    if dense:
+        m.fullattn_fwd(q, k, v, o, lse, causal=causal, stats=fst)
+        m.fullattn_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, causal=causal, stats=bst)
+    else:
+        m.mala_fwd(q, k, v, o, lse, causal=causal, tau=tau, stats=fst)
+        m.mala_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, causal=causal, tau=tau, stats=bst)
+    torch.cuda.synchronize()
+    return {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv,
+            "fdec": fst.decisions.cpu().numpy().astype(np.int8),
+            "bdec": bst.decisions.cpu().numpy().astype(np.int8),
+            "fcnt": fst.counters.cpu().numpy(), "bcnt": bst.counters.cpu().numpy()}
+
+
+def _legal_sel(dec, sel):
+    if sel is None:
+        return dec >= 0
+    m = np.zeros(dec.shape, dtype=bool)
+    for (b, h, i) in sel:
+        m[b, h, i] = dec[b, h, i] >= 0
+    return m
+
+
+def compare_bwd(inp, tau, causal=True, sel_q=None, sel_k=None, fwd_sel=None, label=""):
+    g = run_fwd_bwd(inp, tau, causal)
+    q, k, v, do = (bits_to_f64(inp[x]) for x in ("q", "k", "v", "do"))
+    G = q.shape[1] // k.shape[1]
+    print(f"[bwd {label}] q{q.shape} k{k.shape} tau={tau} causal={causal}", flush=True)
+
+    # --- oracle forward on the GPU's branch of ambiguous tiles ---
+    def fwd(force, flags=O.EXACT):
+        return O.mala_fwd(q, k, v, tau, causal, 64, 64, round_flags=flags, force=force,
+                          sel=fwd_sel)
+
+    ffree = fwd(None)
+    flegal = _legal_sel(ffree["dec"], fwd_sel)
+    fex, fflip = settle_fwd_branch(fwd, g["fdec"], flegal, free=ffree)
+    # the bf16-operand model follows the exact oracle's settled decisions
+    fbf = fwd(fex["dec"].copy(), O.BF16_FWD)
+
+    # --- oracle backward, exact and bf16-operand, on the oracle's forward ---
+    def bwd(o_, lse_, flags, force=None):
+        return O.mala_bwd(q, k, v, o_, lse_, do, tau, causal, 64, 64, round_flags=flags,
+                          force=force, sel_q=sel_q, sel_k=sel_k)
+
+    bfree = bwd(fex["o"], fex["lse"], O.EXACT)
+    legal = bfree["dec"] >= 0
+    gd = g["bdec"]
+    assert (gd[legal] >= 0).all()
+    agree = check_decisions(gd, bfree, legal)
+    dis = legal & (gd != bfree["dec"])
+    force = None
+    if dis.any():
+        mg = bfree["margin"][dis]
+        assert (np.abs(mg) < DELTA).all(), f"backward decision off by margin {mg}"
+        force = np.full(gd.shape, -1, dtype=np.int8)
+        force[dis] = gd[dis]
+        bfree = bwd(fex["o"], fex["lse"], O.EXACT, force)
+    bex = bfree
+    bbf = bwd(fbf["o"], fbf["lse"], O.BF16_BWD, bex["dec"].copy())
+    bmag = bwd(fbf["o"], fbf["lse"], O.BF16_BWD | O.ABS, bex["dec"].copy())
+    bmd = bwd(fbf["o"], fbf["lse"], O.ABS_D, bex["dec"].copy())
+
+    rq = _rows_q(sel_q, q.shape)
+    rk = _rows_k(sel_k, k.shape, G)
+    out = {"agree": agree, "fflip": fflip, "bflip": int(dis.sum())}
+    for name, rows in (("dq", rq), ("dk", rk), ("dv", rk)):
+        x = gpu_to_f64(g[name])[rows]
+        ok, worst = v1_ok(x, bbf[name][rows], bmag[name][rows], bmd[name][rows])
+        assert ok, f"{name} V1 worst ratio {worst}"
+        r2 = v2(x, bbf[name][rows])
+        assert r2 <= V2_TOL, f"{name} V2 {r2}"
+        ok, rl2 = l2_ok(x, bex[name][rows], bmag[name][rows])
+        assert ok, f"{name} relative L2 vs fp64 {rl2}"
+        assert np.isfinite(x).all()
+        out[name + "_v2"] = r2
+        out[name + "_l2"] = rl2
+    # backward support nested in forward support (Sec. 2.2), up to ties
+    viol = (gd == 1) & (g["fdec"] == 0) & _legal_sel(fex["dec"], fwd_sel)
+    if viol.any():
+        fm = fex["margin"][viol]
+        assert np.all(np.abs(fm) < DELTA), "backward retained a tile forward skipped"
+    out["bret"] = float((gd == 1).sum() / max(1, (gd >= 0).sum()))
+    out["g"] = g
+    print({k_: v_ for k_, v_ in out.items() if k_ != "g"}, flush=True)
+    return out
+
+
+def _rows_q(sel, shape):
+    if sel is None:
+        return (slice(None),) * 4
+    B, H, N, d = shape
+    m = np.zeros((B, H, N), dtype=bool)
+    for (b, h, i) in sel:
+        m[b, h, 64 * i:min(N, 64 * i + 64)] = True
+    return np.nonzero(m)
+
+
+def _rows_k(sel, shape, G):
+    if sel is None:
+        return (slice(None),) * 4
+    B, H, N, d = shape
+    m = np.zeros((B, H, N), dtype=bool)
+    for (b, g, j) in sel:
+        m[b, g, 64 * j:min(N, 64 * j + 64)] = True
+    return np.nonzero(m)
+
+
+def _gen(seed, B, Hq, Hkv, N, d, planted, sigma=3.0, local=False):
+    return W.peaked(W.Spec(seed, B, Hq, Hkv, N, d, sigma, planted, local_bias=local))
+
+
+@pytest.mark.parametrize("N,Hq,Hkv,d,tau", [
+    (1, 2, 1, 128, 1.0),
+    (65, 4, 2, 64, 1.0),
+    (200, 2, 2, 128, 1.0),
+    (777, 4, 1, 128, 1.0),      # ragged, GQA 4:1, odd number of key blocks
+    (640, 8, 2, 128, 4.0),
+    (1000, 3, 3, 64, 0.25),
+])
+def test_backward_shapes(N, Hq, Hkv, d, tau):
+    compare_bwd(_gen(300 + N, 1, Hq, Hkv, N, d, 10), tau, label=f"N{N}")
+
+
+def test_backward_batch2_tau_extremes():
+    inp = _gen(11, 2, 4, 2, 333, 128, 6)
+    compare_bwd(inp, 0.0, label="tau0")
+    r = compare_bwd(inp, math.inf, label="tauinf")
+    assert not r["g"]["dq"].any() and not r["g"]["dk"].any() and not r["g"]["dv"].any()
+
+
+def test_backward_noncausal():
+    a = W.peaked(W.Spec(51, 1, 4, 2, 300, 128, 3.0, 0))
+    b = W.peaked(W.Spec(52, 1, 4, 2, 450, 128, 3.0, 8))
+    inp = {"q": a["q"], "do": a["do"], "k": b["k"], "v": b["v"]}
+    compare_bwd(inp, 1.0, causal=False, label="noncausal")
+
+
+def test_backward_dense_identity_and_determinism():
+    inp = _gen(61, 1, 8, 2, 900, 128, 12)
+    a = run_fwd_bwd(inp, 0.0)
+    b = run_fwd_bwd(inp, 0.0, dense=True)
+    c = run_fwd_bwd(inp, 0.0)
+    # dK, dV accumulate in registers: bitwise repeatable and equal to dense
+    assert torch.equal(a["dk"], b["dk"]) and torch.equal(a["dv"], b["dv"])
+    assert torch.equal(a["dk"], c["dk"]) and torch.equal(a["dv"], c["dv"])
+    # dQ sums fp32 atomics in arbitrary order: equal up to rounding
+    assert (a["dq"].float() - c["dq"].float()).abs().max().item() < 1e-2
+
+
+def test_cfg2_forward_backward_full():
+    w = W.cfg2()
+    r = compare_bwd(W.peaked(w.spec), w.tau, label=w.name)
+    print("cfg2 bwd retained", r["bret"])
+
+
+@pytest.mark.parametrize("length", [1024, 4096])
+def test_cfg3_forward_backward(length):
+    w = W.cfg3(length)
+    compare_bwd(W.peaked(w.spec), w.tau, label=w.name)
+
+
+def test_cfg4_backward_sampled():
+    """128K, 8 query / 1 KV head, the launch the benchmark times. The oracle
+    recomputes dQ on sampled query blocks and dK/dV on the last eight key
+    blocks (whose contributing query rows it can afford to run forward)."""
+    w = W.cfg4()
+    inp = W.peaked(w.spec)
+    Tr = w.spec.seqlen // 64
+    qblocks = [0, 1, 700, Tr - 1]
+    sel_q = [(0, h, i) for i in qblocks for h in (0, 3)]
+    tail = range(Tr - 8, Tr)
+    sel_k = [(0, 0, j) for j in tail]
+    fwd_sel = sorted(set(sel_q) | {(0, h, i) for h in range(8) for i in tail})
+    r = compare_bwd(inp, w.tau, sel_q=sel_q, sel_k=sel_k, fwd_sel=fwd_sel, label=w.name)
+    # the sampled key rows must carry gradient, or the check above is empty
+    rk = _rows_k(sel_k, r["g"]["dk"].shape, 8)
+    assert r["g"]["dk"].float().cpu().numpy()[rk].any()

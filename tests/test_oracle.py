@@ -466,3 +466,39 @@ def test_bf16_operand_mode_is_close_to_exact():
     assert np.abs(r["o"] - e["o"]).max() < 2e-2
     assert np.abs(r["o"] - e["o"]).max() > 0
     assert np.abs(r["lse"] - e["lse"]).max() < 1e-5
+
+
+# ------------------------------------------------------- magnitude mode ----
+
+def test_magnitude_mode_bounds_and_matches_twin():
+    q, k, v, do = _tiny_inputs(16, 2, 1, 4, 9)
+    for tau in (0.5, 2.0):
+        r = O.mala_fwd(q, k, v, tau, True, 4, 4)
+        m = O.mala_fwd(q, k, v, tau, True, 4, 4, round_flags=O.ABS, force=r["dec"])
+        assert (np.abs(r["o"]) <= m["o"] + 1e-12).all()          # triangle inequality
+        assert np.array_equal(m["dec"], r["dec"])
+        b = O.mala_bwd(q, k, v, r["o"], r["lse"], do, tau, True, 4, 4)
+        bm = O.mala_bwd(q, k, v, r["o"], r["lse"], do, tau, True, 4, 4, round_flags=O.ABS,
+                        force=b["dec"])
+        tq, tk, tv, _ = twin_bwd(q, k, v, r["o"], r["lse"], do, tau, True, 4, 4, mag=True)
+        for x, mm, t in ((b["dq"], bm["dq"], tq), (b["dk"], bm["dk"], tk), (b["dv"], bm["dv"], tv)):
+            assert (np.abs(x) <= mm + 1e-12).all()
+            assert np.allclose(mm, t, rtol=1e-11, atol=1e-12)
+        bd = O.mala_bwd(q, k, v, r["o"], r["lse"], do, tau, True, 4, 4, round_flags=O.ABS_D,
+                        force=b["dec"])
+        tq, tk, tv, _ = twin_bwd(q, k, v, r["o"], r["lse"], do, tau, True, 4, 4, dsens=True)
+        assert np.allclose(bd["dq"], tq, rtol=1e-11, atol=1e-12)
+        assert np.allclose(bd["dk"], tk, rtol=1e-11, atol=1e-12)
+        assert not bd["dv"].any() and not tv.any()
+
+
+def test_magnitude_mode_equals_value_for_nonnegative_operands():
+    q, k, v, do = _tiny_inputs(14, 2, 2, 4, 4)
+    v, do = np.abs(v), np.abs(do)
+    r = O.mala_fwd(q, k, v, 1.0, True, 2, 2)
+    m = O.mala_fwd(q, k, v, 1.0, True, 2, 2, round_flags=O.ABS, force=r["dec"])
+    assert np.allclose(m["o"], r["o"], rtol=1e-13, atol=1e-13)
+    b = O.mala_bwd(q, k, v, r["o"], r["lse"], do, 1.0, True, 2, 2)
+    bm = O.mala_bwd(q, k, v, r["o"], r["lse"], do, 1.0, True, 2, 2, round_flags=O.ABS,
+                    force=b["dec"])
+    assert np.allclose(bm["dv"], b["dv"], rtol=1e-13, atol=1e-13)

@@ -84,8 +84,11 @@ def twin_fwd(q, k, v, tau, causal=True, bq=64, bk=64, scale=None):
     return o, lse, np.asarray(decs), np.asarray(keeps)
 
 
-def twin_bwd(q, k, v, o, lse, dout, tau, causal=True, bq=64, bk=64, scale=None):
-    """Masked-gradient form of Algorithm 2 -> (dq, dk, dv, dec)."""
+def twin_bwd(q, k, v, o, lse, dout, tau, causal=True, bq=64, bk=64, scale=None, mag=False,
+             dsens=False):
+    """Masked-gradient form of Algorithm 2 -> (dq, dk, dv, dec). With
+    mag=True every product uses absolute values (|dS| |K|, P |dO|, ...);
+    with dsens=True dS is replaced by P * sum_d |O||dO| (and dV is 0)."""
     B, Hq, Nq, d = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
     G = Hq // Hkv
@@ -118,9 +121,14 @@ def twin_bwd(q, k, v, o, lse, dout, tau, causal=True, bq=64, bk=64, scale=None):
             dP = dout[b, h] @ v[b, g].T
             D = (o[b, h] * dout[b, h]).sum(axis=1)
             dS = Pm * (dP - D[:, None])
-            dq[b, h] = scale * dS @ k[b, g]
-            dk[b, g] += scale * dS.T @ q[b, h]
-            dv[b, g] += Pm.T @ dout[b, h]
+            if dsens:
+                dS = Pm * np.abs(o[b, h] * dout[b, h]).sum(axis=1)[:, None]
+                mag = True
+            f = np.abs if mag else (lambda x: x)
+            dq[b, h] = scale * f(dS) @ f(k[b, g])
+            dk[b, g] += scale * f(dS).T @ f(q[b, h])
+            if not dsens:
+                dv[b, g] += Pm.T @ f(dout[b, h])
     return dq, dk, dv, dec
 
 
