@@ -220,10 +220,18 @@ __global__ __launch_bounds__(512, 1) void bwd_main_kernel(BwdParams p) {
   const int i_first = p.causal ? j0 : 0;
   const int n_i = p.tr - i_first;
   const int n_items = n_i > 0 ? p.group * n_i : 0;
+  // Q rows and the LSE of the next item are prefetched into registers one
+  // item ahead (the LDS-only barriers leave those loads in flight)
   bf16x8 qreg[QPT];
+  float lreg = 0.f;
+  auto load_lse = [&](int h, int i) {
+    const int qq = 64 * i + tid;
+    lreg = (tid < 64 && qq < p.nq) ? p.lse[(size_t)(b * p.heads_q + h) * p.nq + qq] : 0.f;
+  };
   if (n_items > 0) {
     const int h = kvh * p.group;
     load_rows(p.q + (size_t)(b * p.heads_q + h) * p.nq * D, i_first, qreg);
+    load_lse(h, i_first);
   }
 
   for (int it = 0; it < n_items; ++it) {
@@ -232,19 +240,20 @@ __global__ __launch_bounds__(512, 1) void bwd_main_kernel(BwdParams p) {
     const int h = kvh * p.group + hh;
     const size_t row0 = (size_t)(b * p.heads_q + h) * p.nq;
 
-    __syncthreads();  // previous item's LDS reads complete
+    lds_barrier();  // previous item's LDS reads complete
     store_rows(qreg, q_lds, qt_lds);
     if (tid < 64) {
       const int qq = 64 * i + tid;
-      const bool ok = qq < p.nq;
-      z_lds[tid] = ok ? p.lse[row0 + qq] * kLog2e : 0.f;
+      z_lds[tid] = lreg * kLog2e;
       const float L = p.causal ? (float)(qq + 1) : (float)p.nk;
       t_lds[tid] = p.log2_tau - log2f(L);  // log2(tau / L_q)
     }
-    __syncthreads();  // Q_i, z, thresholds visible
+    lds_barrier();  // Q_i, z, thresholds visible
     if (it + 1 < n_items) {
       const int hn = kvh * p.group + (it + 1) / n_i;
-      load_rows(p.q + (size_t)(b * p.heads_q + hn) * p.nq * D, i_first + (it + 1) % n_i, qreg);
+      const int in = i_first + (it + 1) % n_i;
+      load_rows(p.q + (size_t)(b * p.heads_q + hn) * p.nq * D, in, qreg);
+      load_lse(hn, in);
     }
 
     const bool part = kb_valid && (!p.causal || i >= jw);
@@ -289,7 +298,7 @@ __global__ __launch_bounds__(512, 1) void bwd_main_kernel(BwdParams p) {
       want = wave_any(want);
     }
     if (lane == 0) flags[w] = want ? 1 : 0;
-    __syncthreads();
+    lds_barrier();
     const bool ret0 = (flags[0] | flags[1] | flags[2] | flags[3]) != 0;
     const bool ret1 = (flags[4] | flags[5] | flags[6] | flags[7]) != 0;
     const bool retain = part && (kb == 0 ? ret0 : ret1);
@@ -321,7 +330,7 @@ __global__ __launch_bounds__(512, 1) void bwd_main_kernel(BwdParams p) {
         for (int r = 0; r < 4; ++r) s[qs][r] = fast_exp2(s[qs][r]);  // P (Alg. 2 step 13)
     }
     store_rows(doreg, do_lds, dot_lds);
-    __syncthreads();  // dO_i, dO_i^T, D_i visible
+    lds_barrier();  // dO_i, dO_i^T, D_i visible
 
     if (retain) {
       // dP = dO V^T (Alg. 2 step 13), same layout as S
@@ -376,7 +385,7 @@ __global__ __launch_bounds__(512, 1) void bwd_main_kernel(BwdParams p) {
               dst[qs >> 1][4 * (qs & 1) + r];
         }
     }
-    __syncthreads();  // dS of both key blocks visible
+    lds_barrier();  // dS of both key blocks visible
 
     // dQ_i += dS K over the retained key blocks (Alg. 2 step 16); wave w
     // computes queries 16(w%4).. and d columns (D/2)(w/4).. of the tile

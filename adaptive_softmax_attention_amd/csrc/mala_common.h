@@ -44,6 +44,21 @@ __device__ __forceinline__ float group4_sum(float x) {
 
 __device__ __forceinline__ bool wave_any(bool p) { return __any(p); }
 
+// Workgroup barrier for LDS traffic only. __syncthreads() also fences global
+// memory at workgroup scope, which makes every wave drain its outstanding
+// global loads (s_waitcnt vmcnt(0)) at each barrier and so defeats register
+// prefetching. None of these kernels communicates through global memory
+// within a launch, so waiting for this wave's LDS operations
+// (lgkmcnt(0), with vmcnt and expcnt left at their maxima) before s_barrier
+// is sufficient; the signal fence keeps the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // Round-to-nearest-even fp32 -> bf16 pair (the compiler emits the native
 // conversion on gfx950).
 __device__ __forceinline__ __bf16 to_bf16(float x) { return static_cast<__bf16>(x); }

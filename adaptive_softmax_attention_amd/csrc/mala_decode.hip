@@ -166,7 +166,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecParams p) {
           for (int r = 0; r < 4; ++r) p_lds[16 * ks + 4 * g4 + r][l16] = sc[ks][r];
         if (g4 == 0) a_lds[l16] = alpha;
       }
-      __syncthreads();
+      lds_barrier();
       float al[GM];
 #pragma unroll
       for (int h = 0; h < GM; ++h) al[h] = a_lds[h];
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecParams p) {
           for (int h = 0; h < GM; ++h) acc[h][e] += pk[h] * ve;
         }
       }
-      __syncthreads();
+      lds_barrier();
     }
   }
   // reduce the key phases, then write this split's partial (m, l, u)

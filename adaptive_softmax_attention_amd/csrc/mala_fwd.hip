@@ -138,7 +138,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   load_k(jtop);
   for (int j = jtop; j >= 0; --j) {
     store_k();
-    __syncthreads();  // K_j visible; previous tile's LDS reads complete
+    lds_barrier();  // K_j visible; previous tile's LDS reads complete
     if (j > 0) load_k(j - 1);
 
     const bool part = valid && j <= jmax;
@@ -210,7 +210,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
       }
     }
     if (lane == 0) flags[w] = retain ? 1 : 0;
-    __syncthreads();
+    lds_barrier();
     // block decision = either half wants it; V is needed if any block retains
     retain = part && (flags[2 * blk] | flags[2 * blk + 1]) != 0;
     int anyf = 0;
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
         *dst = vreg[0][e];
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (part && retain) {
       // O^T += V^T P^T (Alg. 1 step 17)
 #pragma unroll

@@ -210,7 +210,19 @@ def test_cfg4_backward_sampled():
     tail = range(Tr - 8, Tr)
     sel_k = [(0, 0, j) for j in tail]
     fwd_sel = sorted(set(sel_q) | {(0, h, i) for h in range(8) for i in tail})
-    r = compare_bwd(inp, w.tau, sel_q=sel_q, sel_k=sel_k, fwd_sel=fwd_sel, label=w.name)
-    # the sampled key rows must carry gradient, or the check above is empty
-    rk = _rows_k(sel_k, r["g"]["dk"].shape, 8)
-    assert r["g"]["dk"].float().cpu().numpy()[rk].any()
+    # (at this length every backward tile touching the last key blocks is
+    # skipped, so their dK/dV are zero on both sides: this part confirms no
+    # spurious contribution; the full dK/dV comparison of this head layout
+    # runs at 8K below)
+    compare_bwd(inp, w.tau, sel_q=sel_q, sel_k=sel_k, fwd_sel=fwd_sel, label=w.name)
+
+
+def test_cfg4_layout_8k_full():
+    """The 128K workload's head layout (8 query / 1 KV head, d 128, 256 planted
+    pairs' density) at 8K, every output compared."""
+    w = W.cfg4()
+    s = w.spec
+    inp = W.peaked(W.Spec(s.seed, 1, 8, 1, 8192, 128, s.sigma_s, 16))
+    r = compare_bwd(inp, w.tau, label="cfg4-layout-8k")
+    g = r["g"]
+    assert g["dk"].abs().sum().item() > 0 and g["dv"].abs().sum().item() > 0
