@@ -63,6 +63,66 @@ __device__ __forceinline__ void lds_barrier() {
 // conversion on gfx950).
 __device__ __forceinline__ __bf16 to_bf16(float x) { return static_cast<__bf16>(x); }
 
+// --- asynchronous global -> LDS copies ---------------------------------------
+// global_load_lds_dwordx4: each lane's 16 bytes land at M0 + 16 * lane
+// (lane-contiguous); the global address per lane is free, so a swizzled LDS
+// layout is produced by choosing which chunk each lane fetches. The copy
+// counts in vmcnt; vmcnt_wait<N>() waits until at most N vector-memory
+// operations of this wave are outstanding (loads complete in issue order).
+// The copy is issued as inline assembly: the compiler then neither treats it
+// as an LDS store (it would otherwise drain vmcnt before every later LDS
+// read, since it cannot tell ring slots apart) nor counts it, which only
+// strengthens the waits it emits for its own loads. All ordering between the
+// copies and the LDS reads of their data is explicit: vmcnt_wait followed by
+// lds_barrier.
+__device__ __forceinline__ void async_copy16(const void* gsrc, void* lds_base) {
+  // the LDS base is wave-uniform (M0); make that explicit to the compiler
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_base);
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(gsrc), "s"(lds)
+      : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void vmcnt_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (7 << 4) | (0xF << 8));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// vmcnt wait with a run-time count in 0..4 (branches to constant waits).
+__device__ __forceinline__ void vmcnt_wait_le(int n) {
+  if (n <= 0) vmcnt_wait<0>();
+  else if (n == 1) vmcnt_wait<1>();
+  else if (n == 2) vmcnt_wait<2>();
+  else if (n == 3) vmcnt_wait<3>();
+  else vmcnt_wait<4>();
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+// i % 4 of the 8-byte rows addressed by lanes 4e + i/4 (e = 0..3). Lane j
+// addressing row k0 + j/4, columns n0 + 4(j%4) .. +3 of a row-major [k][n]
+// bf16 tile therefore gives lane i the column n0 + i for rows k0 .. k0+3:
+// the transposed MFMA operand, read straight from the natural layout.
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short short4v;
+__device__ __forceinline__ short4v lds_read_tr4(const __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) short4v*)(p));
+}
+// Two transposed 4-element reads joined into one MFMA operand. The join is a
+// whole-vector shuffle plus one bit cast: inserting the 16-bit values into a
+// bf16 vector element by element produced wrong operands at -O3.
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short short8v;
+__device__ __forceinline__ bf16x8 join_tr(const short4v& lo, const short4v& hi) {
+  const short8v v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // --- LDS swizzles -----------------------------------------------------------
 // K tile in LDS: [64 keys][D] bf16, 16-byte chunks XOR-swizzled per key so
 // that the eight lanes of one read phase (keys 0-3 and 8-11 of a 16-key
@@ -72,5 +132,8 @@ __device__ __forceinline__ int k_swz(int key) {
 }
 // V^T tile in LDS: [D][64 keys] bf16 (128 B rows of eight 16-byte chunks).
 __device__ __forceinline__ int v_swz(int d) { return (d ^ (d >> 3)) & 7; }
+// Row-major tiles read with the transposing read (4 consecutive rows x 2
+// chunks per 16-lane group): even row offsets keep the 8 chunks distinct.
+__device__ __forceinline__ int tr_swz(int row) { return (row << 1) ^ ((row >> 3) & 1); }
 
 }  // namespace mala

@@ -10,15 +10,20 @@
 //     synchronisation;
 //   * a workgroup of 8 waves holds 4 blocks that share K/V tiles: 4 query
 //     heads of one KV head (GQA), or 2 heads x 2 blocks, or 4 consecutive
-//     query blocks of one head; K/V tiles are staged once in LDS for all 4;
+//     query blocks of one head;
 //   * scores are formed transposed, S^T = K Q^T (16x16x32 bf16 MFMA, fp32
 //     accumulate), so each lane holds 16 keys of one query column: the row
 //     max and row sum need only 2 cross-lane steps, and P^T is already in
 //     the B-operand layout of O^T = V^T P^T;
-//   * key blocks are visited from the diagonal down (Sec. 2.2); K of the next
-//     tile is prefetched into registers while the current tile computes; V is
-//     fetched only after the ballot says some wave of the group retains the
-//     tile, and its load latency overlaps the exp / rescale of P;
+//   * K and V tiles are copied asynchronously from global memory straight
+//     into LDS rings (global_load_lds, row-major, swizzled); V^T operands are
+//     read with the transposing LDS read, so nothing is staged in registers;
+//   * software pipeline over the key blocks, visited from the diagonal down
+//     (Sec. 2.2): K runs two tiles ahead; a tile's V is requested only after
+//     the ballot says some block retains it, and is consumed one iteration
+//     later: the running (m, l) update of a tile needs only its scores, so
+//     the next tile's score discovery proceeds while V is in flight, and
+//     O <- alpha O + P V is applied a step late in the same order;
 //   * workgroups are issued longest-first (largest query block first).
 #include "mala_common.h"
 #include "mala_internal.h"
@@ -46,16 +51,17 @@ struct FwdParams {
 
 template <int D, bool kTest>
 __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
-  constexpr int NDC = D / 32;          // 32-wide reduction chunks over d
-  constexpr int NDS = D / 16;          // 16-row subtiles of O^T over d
-  constexpr int KCH = D / 8;           // 16-byte chunks per K / V row
-  constexpr int NT = 512;              // threads per workgroup
-  constexpr int NQS = 2;               // 16-query subtiles per wave (32 rows)
-  constexpr int KLD = 64 * KCH / NT;   // 16-byte K loads per thread
-  constexpr int KPT = 64 * KCH / NT;   // keys per thread in the V transpose
+  constexpr int NDC = D / 32;         // 32-wide reduction chunks over d
+  constexpr int NDS = D / 16;         // 16-row subtiles of O^T over d
+  constexpr int KCH = D / 8;          // 16-byte chunks per K / V row
+  constexpr int NT = 512;             // threads per workgroup
+  constexpr int NQS = 2;              // 16-query subtiles per wave (32 rows)
+  constexpr int CPT = 64 * KCH / NT;  // async 16-byte copies per thread per tile
+  constexpr int RK = 3;               // K ring: current tile + 2 ahead
+  constexpr int RV = 2;               // V ring
 
-  __shared__ __attribute__((aligned(16))) __bf16 k_lds[64 * D];
-  __shared__ __attribute__((aligned(16))) __bf16 vt_lds[D * 64];
+  __shared__ __attribute__((aligned(16))) __bf16 k_ring[RK][64 * D];
+  __shared__ __attribute__((aligned(16))) __bf16 v_ring[RV][64 * D];
   __shared__ int flags[8];
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
@@ -74,8 +80,8 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   const int h = kvh * p.group + hg * p.hpw + (blk % p.hpw);
   const int i = ig * p.ipw + (blk / p.hpw);
   const bool valid = i < p.tr;
-  const int q0 = i * 64 + 32 * half;      // first row of this wave
-  const int bq0 = i * 64;                 // first row of the block
+  const int q0 = i * 64 + 32 * half;  // first row of this wave
+  const int bq0 = i * 64;             // first row of the block
   const int jmax = valid ? (p.causal ? i : p.tc - 1) : -1;
   const int i_top = min(ig * p.ipw + p.ipw - 1, p.tr - 1);
   const int jtop = p.causal ? i_top : p.tc - 1;
@@ -113,36 +119,70 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
     for (int ds = 0; ds < NDS; ++ds) oacc[ds][qs] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // ---- K tile staging: global -> registers -> swizzled LDS ----
-  uint4 kreg[KLD];
-  auto load_k = [&](int j) {
+  // ---- async tile copies (rows past the end re-read the last row; those
+  //      keys are masked, so only finite values reach the products) ----
+  auto issue_tile = [&](const __bf16* base, int j, __bf16* slot, bool tr_layout) {
 #pragma unroll
-    for (int x = 0; x < KLD; ++x) {
-      const int c = tid + NT * x, row = c / KCH, ch = c % KCH;
-      const int key = j * 64 + row;
-      if (key < p.nk)
-        kreg[x] = *(const uint4*)(kbase + (size_t)key * D + ch * 8);
-      else
-        kreg[x] = uint4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto store_k = [&]() {
-#pragma unroll
-    for (int x = 0; x < KLD; ++x) {
-      const int c = tid + NT * x, row = c / KCH, ch = c % KCH;
-      const int sw = ch ^ (k_swz(row) & (KCH - 1));
-      *(uint4*)(k_lds + row * D + sw * 8) = kreg[x];
+    for (int x = 0; x < CPT; ++x) {
+      const int s0 = x * NT + w * 64;  // first 16-byte slot of this wave
+      const int s = s0 + lane;
+      const int row = s / KCH, pc = s % KCH;
+      const int sw = tr_layout ? (tr_swz(row) & (KCH - 1)) : (k_swz(row) & (KCH - 1));
+      const int key = min(j * 64 + row, p.nk - 1);
+      async_copy16(base + (size_t)key * D + (pc ^ sw) * 8, slot + s0 * 8);
     }
   };
 
-  load_k(jtop);
+  // pending post-score work of the previous tile (applied one step late)
+  bool pend = false;
+  bf16x8 pend_pb[2][NQS];
+  float pend_alpha[NQS];
+  bool v_prev = false;  // V of the previous tile was requested
+
+  auto apply_pv = [&](const __bf16* vt) {
+    // O^T <- alpha O^T + V^T P^T (Alg. 1 step 17)
+#pragma unroll
+    for (int qs = 0; qs < NQS; ++qs)
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        oacc[ds][qs][0] *= pend_alpha[qs];
+        oacc[ds][qs][1] *= pend_alpha[qs];
+        oacc[ds][qs][2] *= pend_alpha[qs];
+        oacc[ds][qs][3] *= pend_alpha[qs];
+      }
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        // lane addresses row k0 + l16/4, columns 16ds + 4(l16%4): the
+        // transposing read returns V[k0 + e][16ds + l16], e = 0..3
+        short4v t[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int row = 32 * kc + 8 * g4 + 4 * hh + (l16 >> 2);
+          const int col = 16 * ds + 4 * (l16 & 3);
+          const int ch = col >> 3;
+          t[hh] = lds_read_tr4(vt + row * D + ((ch ^ (tr_swz(row) & (KCH - 1))) * 8) + (col & 7));
+        }
+        const bf16x8 a = join_tr(t[0], t[1]);
+#pragma unroll
+        for (int qs = 0; qs < NQS; ++qs)
+          oacc[ds][qs] = mfma16x16x32(a, pend_pb[kc][qs], oacc[ds][qs]);
+      }
+  };
+
+  // prologue: K of the first two tiles
+  issue_tile(kbase, jtop, k_ring[jtop % RK], false);
+  if (jtop >= 1) issue_tile(kbase, jtop - 1, k_ring[(jtop - 1) % RK], false);
+
   for (int j = jtop; j >= 0; --j) {
-    store_k();
-    lds_barrier();  // K_j visible; previous tile's LDS reads complete
-    if (j > 0) load_k(j - 1);
+    // K_j complete; V_{j+1} and K_{j-1} may still be in flight
+    vmcnt_wait_le((v_prev ? CPT : 0) + (j >= 1 ? CPT : 0));
+    lds_barrier();
+    const __bf16* kt = k_ring[j % RK];
 
     const bool part = valid && j <= jmax;
-    bool retain = false;
+    bool want = false;
     floatx4 s[4][NQS];
     float mt[NQS];
     if (part) {
@@ -159,7 +199,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
           // so output lane group g4 ends up with 8 consecutive keys per 32
           const int kr = 32 * (ks >> 1) + 8 * (l16 >> 2) + 4 * (ks & 1) + (l16 & 3);
           const int ch = 4 * dc + g4;
-          const bf16x8 a = *(const bf16x8*)(k_lds + kr * D + ((ch ^ (k_swz(kr) & (KCH - 1))) * 8));
+          const bf16x8 a = *(const bf16x8*)(kt + kr * D + ((ch ^ (k_swz(kr) & (KCH - 1))) * 8));
 #pragma unroll
           for (int qs = 0; qs < NQS; ++qs) s[ks][qs] = mfma16x16x32(a, qr[qs][dc], s[ks][qs]);
         }
@@ -191,7 +231,6 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
       if constexpr (kTest) {
         // Eq. 3 in log2 units: skip iff every valid row with a legal key has
         // rowmax*c - m - log2(l) < log2(tau/L); l = 0 counts as +inf
-        bool want = false;
 #pragma unroll
         for (int qs = 0; qs < NQS; ++qs) {
           const int qq = q0 + 16 * qs + l16;
@@ -204,15 +243,17 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
             }
           }
         }
-        retain = wave_any(want);
+        want = wave_any(want);
       } else {
-        retain = true;
+        want = true;
       }
     }
-    if (lane == 0) flags[w] = retain ? 1 : 0;
+    if (lane == 0) flags[w] = want ? 1 : 0;
+    // V_{j+1} complete (K_{j-1} may stay in flight); flags visible
+    if (v_prev) vmcnt_wait_le(j >= 1 ? CPT : 0);
     lds_barrier();
     // block decision = either half wants it; V is needed if any block retains
-    retain = part && (flags[2 * blk] | flags[2 * blk + 1]) != 0;
+    const bool retain = part && (flags[2 * blk] | flags[2 * blk + 1]) != 0;
     int anyf = 0;
 #pragma unroll
     for (int x = 0; x < 8; ++x) anyf |= flags[x];
@@ -227,24 +268,21 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
       if (p.decisions)
         p.decisions[((size_t)(b * p.heads_q + h) * p.tr + i) * p.tc + j] = retain ? 1 : 0;
     }
-    if (anyf == 0) continue;  // whole tile skipped by every block: V never read
-
-    // ---- V_j load (some wave retains), overlapped with the softmax update ----
-    bf16x8 vreg[KPT];
-    const int vch = tid % KCH, vkg = tid / KCH;
-#pragma unroll
-    for (int x = 0; x < KPT; ++x) {
-      const int key = j * 64 + vkg * KPT + x;
-      if (key < p.nk)
-        vreg[x] = *(const bf16x8*)(vbase + (size_t)key * D + vch * 8);
-      else
-        vreg[x] = bf16x8{};
+    // the previous tile's P V (its V arrived during this tile's scoring)
+    if (pend) apply_pv(v_ring[(j + 1) % RV]);
+    // request V_j only if some block retains tile j (skipped tiles never
+    // touch V), then K two tiles ahead
+    if (anyf) {
+      issue_tile(vbase, j, v_ring[j % RV], true);
+      if (tid == 0 && p.counters) atomicAdd(&p.counters[3], 1ull);
     }
-    if (tid == 0 && p.counters) atomicAdd(&p.counters[3], 1ull);
+    if (j >= 2) issue_tile(kbase, j - 2, k_ring[(j - 2) % RK], false);
+    v_prev = anyf != 0;
 
-    bf16x8 pb[2][NQS];
-    if (part && retain) {
-      // online-softmax update of every valid row (Alg. 1 steps 14-18)
+    pend = retain;
+    if (retain) {
+      // online-softmax update of every valid row (Alg. 1 steps 14-18); the
+      // O update for this tile is applied next iteration
 #pragma unroll
       for (int qs = 0; qs < NQS; ++qs) {
         const float mn = fmaxf(m2[qs], mt[qs] * p.c);
@@ -262,13 +300,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
         rs = group4_sum(rs);
         lsum[qs] = alpha * lsum[qs] + rs;
         m2[qs] = mn;
-#pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) {
-          oacc[ds][qs][0] *= alpha;
-          oacc[ds][qs][1] *= alpha;
-          oacc[ds][qs][2] *= alpha;
-          oacc[ds][qs][3] *= alpha;
-        }
+        pend_alpha[qs] = alpha;
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
           bf16x8 t;
@@ -277,49 +309,15 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
             t[r] = to_bf16(s[2 * kc][qs][r]);
             t[4 + r] = to_bf16(s[2 * kc + 1][qs][r]);
           }
-          pb[kc][qs] = t;
+          pend_pb[kc][qs] = t;
         }
       }
-    }
-    // V^T into LDS: thread holds keys vkg*KPT.. for 8 d values
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = vch * 8 + e;
-      const int key0 = vkg * KPT;
-      const int ch = key0 >> 3, off = key0 & 7;
-      __bf16* dst = vt_lds + d * 64 + ((ch ^ v_swz(d)) * 8) + off;
-      if constexpr (KPT == 4) {
-        bf16x4 t4;
-        t4[0] = vreg[0][e];
-        t4[1] = vreg[1][e];
-        t4[2] = vreg[2][e];
-        t4[3] = vreg[3][e];
-        *(bf16x4*)dst = t4;
-      } else if constexpr (KPT == 2) {
-        typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
-        bf16x2 t2;
-        t2[0] = vreg[0][e];
-        t2[1] = vreg[1][e];
-        *(bf16x2*)dst = t2;
-      } else {
-        *dst = vreg[0][e];
-      }
-    }
-    lds_barrier();
-    if (part && retain) {
-      // O^T += V^T P^T (Alg. 1 step 17)
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) {
-          const int d = 16 * ds + l16;
-          const int ch = 4 * kc + g4;
-          const bf16x8 a = *(const bf16x8*)(vt_lds + d * 64 + ((ch ^ v_swz(d)) * 8));
-#pragma unroll
-          for (int qs = 0; qs < NQS; ++qs) oacc[ds][qs] = mfma16x16x32(a, pb[kc][qs], oacc[ds][qs]);
-        }
     }
   }
+  // the last tile's P V
+  vmcnt_wait<0>();
+  lds_barrier();
+  if (pend) apply_pv(v_ring[0]);
 
   // ---- finalisation (Alg. 1 steps 20-21): O = O / l, LSE = m + log l ----
   if (valid) {
