@@ -1,9 +1,10 @@
-// MALA fused backward (paper Appendix A, Algorithm 2; Sec. 2.2 Eq. 4;
-// Appendix A.1 "Fused backward execution") and the dense FullAttn backward
+// MALA fused backward ("MassAlloc Attention: Let Attention Allocate Its Own Compute":
+// Sec. 2.2 Eq. 4, Appendix A Algorithm 2, and the backward part of
+// Appendix A.1) and the dense FullAttn backward
 // from the same template with the test compiled out.
 //
 // Three kernels on the caller's stream:
-//   1. bwd_pre:  D_q = rowsum(O o dO) in fp32 (Alg. 2 step 14, from the
+//   1. bwd_pre:  D_q = rowsum(O o dO) in fp32 (from the
 //                stored O) and a zero fill of the fp32 dQ accumulator (a fill
 //                kernel rather than a memset, so the sequence can be captured
 //                in a graph);
@@ -11,7 +12,7 @@
 //                64-key blocks (j0 = 2J, j1 = 2J + 1) of one KV head; each wave
 //                owns a 16-key slice and keeps its dK, dV accumulators in
 //                registers. It visits the G query heads of the group and the
-//                query blocks from the diagonal up (Alg. 2 step 5). Per tile:
+//                query blocks from the diagonal up. Per tile:
 //                S = Q K^T is recomputed (16x16x32 bf16 MFMA), the offline test
 //                of Eq. 4 compares every legal s - z_q with log(tau/L_q) against
 //                the forward's LSE (wave ballot, OR over the block's 4 waves at
@@ -260,7 +261,7 @@ __global__ __launch_bounds__(512, 1) void bwd_main_kernel(BwdParams p) {
     bool want = false;
     floatx4 s[4];
     if (part) {
-      // S = Q_i K_j^T recomputed (Alg. 2 step 8); MFMA row R of query
+      // S = Q_i K_j^T recomputed; MFMA row R of query
       // subtile qs holds query 32(qs/2) + 8(R/4) + 4(qs%2) + R%4
 #pragma unroll
       for (int qs = 0; qs < 4; ++qs) s[qs] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -315,7 +316,7 @@ __global__ __launch_bounds__(512, 1) void bwd_main_kernel(BwdParams p) {
     }
     if (!ret0 && !ret1) continue;  // both tiles skipped: dO never loaded
 
-    // ---- retained: dO_i and D_i (Alg. 2 step 12) ----
+    // ---- retained: dO_i and D_i ----
     bf16x8 doreg[QPT];
     load_rows(p.dout + row0 * D, i, doreg);
     if (tid == 0 && p.counters) atomicAdd(&p.counters[3], 1ull);
@@ -327,13 +328,13 @@ __global__ __launch_bounds__(512, 1) void bwd_main_kernel(BwdParams p) {
 #pragma unroll
       for (int qs = 0; qs < 4; ++qs)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s[qs][r] = fast_exp2(s[qs][r]);  // P (Alg. 2 step 13)
+        for (int r = 0; r < 4; ++r) s[qs][r] = fast_exp2(s[qs][r]);  // P
     }
     store_rows(doreg, do_lds, dot_lds);
     lds_barrier();  // dO_i, dO_i^T, D_i visible
 
     if (retain) {
-      // dP = dO V^T (Alg. 2 step 13), same layout as S
+      // dP = dO V^T, same layout as S
       floatx4 dp[4];
 #pragma unroll
       for (int qs = 0; qs < 4; ++qs) dp[qs] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -347,7 +348,7 @@ __global__ __launch_bounds__(512, 1) void bwd_main_kernel(BwdParams p) {
           dp[qs] = mfma16x16x32(a, vreg[dc], dp[qs]);
         }
       }
-      // dS = P o (dP - D) (Alg. 2 step 14); pack P^T and dS^T as A operands
+      // dS = P o (dP - D); pack P^T and dS^T as A operands
       bf16x8 pt[2], dst[2];
 #pragma unroll
       for (int qs = 0; qs < 4; ++qs) {
@@ -362,7 +363,7 @@ __global__ __launch_bounds__(512, 1) void bwd_main_kernel(BwdParams p) {
           dst[qs >> 1][4 * (qs & 1) + r] = to_bf16(dsv);
         }
       }
-      // dV += P^T dO, dK += dS^T Q (Alg. 2 step 15)
+      // dV += P^T dO, dK += dS^T Q
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
@@ -387,7 +388,7 @@ __global__ __launch_bounds__(512, 1) void bwd_main_kernel(BwdParams p) {
     }
     lds_barrier();  // dS of both key blocks visible
 
-    // dQ_i += dS K over the retained key blocks (Alg. 2 step 16); wave w
+    // dQ_i += dS K over the retained key blocks; wave w
     // computes queries 16(w%4).. and d columns (D/2)(w/4).. of the tile
     {
       const int qsd = w & 3, dh = w >> 2;
@@ -418,7 +419,7 @@ __global__ __launch_bounds__(512, 1) void bwd_main_kernel(BwdParams p) {
     }
   }
 
-  // ---- dK_j = scale * sum, dV_j (Alg. 2 step 18); rows = keys 4g4 + r ----
+  // ---- dK_j = scale * sum, dV_j; rows = keys 4g4 + r ----
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int kk = 64 * jw + 16 * kw + 4 * g4 + r;

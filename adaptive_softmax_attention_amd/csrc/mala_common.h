@@ -87,6 +87,19 @@ __device__ __forceinline__ void async_copy16(const void* gsrc, void* lds_base) {
       : "v"(gsrc), "s"(lds)
       : "memory", "m0");
 }
+// 4-byte variant (one dword per lane, lane-contiguous at M0 + 4 * lane).
+__device__ __forceinline__ void async_copy4(const void* gsrc, void* lds_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_base);
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, off"
+      :
+      : "v"(gsrc), "s"(lds)
+      : "memory", "m0");
+}
+
 template <int N>
 __device__ __forceinline__ void vmcnt_wait() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -95,13 +108,19 @@ __device__ __forceinline__ void vmcnt_wait() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// vmcnt wait with a run-time count in 0..4 (branches to constant waits).
+// vmcnt wait with a run-time (wave-uniform) count: branches to the constant
+// wait for the largest supported count <= n (waiting for more is safe).
 __device__ __forceinline__ void vmcnt_wait_le(int n) {
   if (n <= 0) vmcnt_wait<0>();
   else if (n == 1) vmcnt_wait<1>();
   else if (n == 2) vmcnt_wait<2>();
   else if (n == 3) vmcnt_wait<3>();
-  else vmcnt_wait<4>();
+  else if (n < 8) vmcnt_wait<4>();
+  else if (n < 16) vmcnt_wait<8>();
+  else if (n < 18) vmcnt_wait<16>();
+  else if (n < 20) vmcnt_wait<18>();
+  else if (n < 21) vmcnt_wait<20>();
+  else vmcnt_wait<21>();
 }
 
 // ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element

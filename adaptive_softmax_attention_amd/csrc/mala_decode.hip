@@ -1,12 +1,14 @@
-// MALA split-KV decode (paper Sec. 2.4; Appendix A.1 "Fused decoding
-// execution") and the dense split-KV decode with the test compiled out.
+// MALA split-KV decode ("MassAlloc Attention: Let Attention Allocate Its Own Compute":
+// Sec. 2.4 and the decoding part of Appendix A.1) and the dense split-KV
+// decode with the test compiled out.
 //
 // One new query per sequence sees all seqlen_k cached keys (L = seqlen_k,
 // Sec. 2.1). The Tc key tiles are cut into S ranges of ceil(Tc/S) tiles; each
 // (sequence, KV head, split) is an independent chain that starts with fresh
 // (m, l), visits its tiles last-to-first and applies the forward rule to each
 // query head of the group against its own partial normaliser. A second
-// kernel merges the partial (m, l, u) (the review's merge identity).
+// kernel merges the partial (m, l, u) with the identity of "Why exact
+// attention does not need a quadratic matrix" (Method/Mechanism).
 //
 // Memory-bound design (gfx950):
 //   * one wave64 per chain; the G query heads of the KV group share every K
@@ -138,7 +140,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecParams p) {
         const int key = j * 64 + kph + KPH * t;
         vr[t] = key < p.nk ? *(const bf16x8*)(vbase + (size_t)key * D + 8 * dg) : bf16x8{};
       }
-      // online-softmax update of the retaining heads (Alg. 1 steps 14-18)
+      // online-softmax update of the retaining heads
       float alpha = 1.f;
       if (want) {
         const float mn = fmaxf(m2, mt * p.c);
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecParams p) {
       for (int h = 0; h < GM; ++h)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] *= al[h];
-      // u += P V over this lane's key phase (Alg. 1 step 17)
+      // u += P V over this lane's key phase
 #pragma unroll
       for (int t = 0; t < KT; ++t) {
         const int key = kph + KPH * t;

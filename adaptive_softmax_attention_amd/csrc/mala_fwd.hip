@@ -1,5 +1,6 @@
-// MALA fused forward (paper Appendix A, Algorithm 1; Sec. 2.2 Eqs. 1-3;
-// Appendix A.1 "Fused forward execution") and the dense FullAttn forward
+// MALA fused forward ("MassAlloc Attention: Let Attention Allocate Its Own Compute":
+// Sec. 2.2 Eqs. 1-3, Appendix A Algorithm 1, and the forward part of
+// Appendix A.1) and the dense FullAttn forward
 // from the same template with the test compiled out.
 //
 // Work decomposition (gfx950):
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   bool v_prev = false;  // V of the previous tile was requested
 
   auto apply_pv = [&](const __bf16* vt) {
-    // O^T <- alpha O^T + V^T P^T (Alg. 1 step 17)
+    // O^T <- alpha O^T + V^T P^T
 #pragma unroll
     for (int qs = 0; qs < NQS; ++qs)
 #pragma unroll
@@ -186,7 +187,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
     floatx4 s[4][NQS];
     float mt[NQS];
     if (part) {
-      // score discovery (Alg. 1 step 8), every legal tile
+      // score discovery, every legal tile
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
@@ -218,7 +219,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
               if (key >= p.nk || (p.causal && key > qq)) s[ks][qs][r] = -INFINITY;
             }
       }
-      // tile row maxima (Alg. 1 step 9)
+      // tile row maxima
 #pragma unroll
       for (int qs = 0; qs < NQS; ++qs) {
         float x = -INFINITY;
@@ -281,7 +282,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
 
     pend = retain;
     if (retain) {
-      // online-softmax update of every valid row (Alg. 1 steps 14-18); the
+      // online-softmax update of every valid row; the
       // O update for this tile is applied next iteration
 #pragma unroll
       for (int qs = 0; qs < NQS; ++qs) {
@@ -319,7 +320,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   lds_barrier();
   if (pend) apply_pv(v_ring[0]);
 
-  // ---- finalisation (Alg. 1 steps 20-21): O = O / l, LSE = m + log l ----
+  // ---- finalisation: O = O / l, LSE = m + log l ----
   if (valid) {
 #pragma unroll
     for (int qs = 0; qs < NQS; ++qs) {

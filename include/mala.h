@@ -96,8 +96,8 @@ typedef struct {
   uint8_t* decisions;
 } mala_stats;
 
-/* MALA forward (Algorithm 1; Eqs. 1-3; Appendix A.1 "Fused forward
- * execution"). Per (batch, query head, query block), key blocks holding a
+/* MALA forward (Algorithm 1; Eqs. 1-3; the forward part of Appendix A.1).
+ * Per (batch, query head, query block), key blocks holding a
  * legal key are visited from the last one (the diagonal when causal) down to
  * block 0. Each tile is scored; it is skipped when every valid query row with
  * a legal key in it has rowmax - m - log l < log(tau / L_q); otherwise V is
@@ -116,8 +116,8 @@ int fullattn_fwd(const mala_shape* shape, const mala_config* cfg, const void* q,
  * shape or config. */
 size_t mala_bwd_workspace_bytes(const mala_shape* shape, const mala_config* cfg);
 
-/* MALA backward (Algorithm 2; Eq. 4; Appendix A.1 "Fused backward
- * execution"). Key-major: per (batch, KV head, key block), query blocks are
+/* MALA backward (Algorithm 2; Eq. 4; the backward part of Appendix A.1).
+ * Key-major: per (batch, KV head, key block), query blocks are
  * visited for every query head of the group. Q.K is recomputed; a tile is
  * skipped when every legal entry has s - z_q < log(tau / L_q), with z = the
  * forward's LSE; otherwise P = exp(s - z), dP = dO V^T,
@@ -143,7 +143,7 @@ size_t mala_decode_workspace_bytes(const mala_shape* shape, int32_t num_splits);
  * depend on the split count, so callers comparing runs must fix it). */
 int32_t mala_decode_default_splits(const mala_shape* shape);
 
-/* Split-KV MALA decode (Sec. 2.4; Appendix A.1 "Fused decoding execution").
+/* Split-KV MALA decode (Sec. 2.4; the decoding part of Appendix A.1).
  * One new query per sequence: q, o are [batch][heads_q][head_dim], lse is
  * [batch][heads_q]; k_cache, v_cache are [batch][heads_kv][seqlen_k][head_dim]
  * and include the current token (L = seqlen_k, Sec. 2.1). shape->seqlen_q

@@ -16,7 +16,7 @@
  *   - forward procedure: Appendix A, Algorithm 1
  *   - offline backward test, Eq. (4): Sec. 2.2
  *   - backward procedure: Appendix A, Algorithm 2
- *   - split-KV decode: Sec. 2.4 and Appendix A.1 "Fused decoding execution"
+ *   - split-KV decode: Sec. 2.4 and the decoding part of Appendix A.1
  *   - (m, l, u) merge: the review's "Method/Mechanism" section
  *   - dense attention: Sec. 2.1 (FullAttn), the review's first paragraph of
  *     "Method/Mechanism"
@@ -255,7 +255,7 @@ static void online_block(const orc_problem* p, const double* q, int64_t q_stride
   }
   for (int64_t j = j_hi; j >= j_lo; --j) {
     const int64_t k0 = j * bk;
-    /* score discovery with the causal mask (Alg. 1, steps 7-9) */
+    /* score discovery with the causal mask, then the tile row maxima */
     for (int64_t r = 0; r < nrows; ++r) {
       mt[r] = -INFINITY;
       for (int c = 0; c < bk; ++c) {
@@ -291,7 +291,7 @@ static void online_block(const orc_problem* p, const double* q, int64_t q_stride
     if (dec) dec[j] = retain ? ORC_RETAIN : ORC_SKIP;
     if (mrg) mrg[j] = tile_margin;
     if (!retain) continue; /* m, l, O unchanged */
-    /* online-softmax update of every valid row (Alg. 1, steps 13-18) */
+    /* retained tile: online-softmax update of every valid row */
     for (int64_t r = 0; r < nrows; ++r) {
       const double m_new = mt[r] > m[r] ? mt[r] : m[r];
       if (m_new == -INFINITY) continue;
@@ -356,7 +356,7 @@ int orc_mala_fwd(const orc_problem* p, const double* q, const double* k, const d
                  k + (b * p->heads_kv + g) * Nk * d, v + (b * p->heads_kv + g) * Nk * d, q0,
                  nrows, 0, last_key_block(p, q1), force ? force + tile_base : NULL,
                  dec ? dec + tile_base : NULL, mrg ? mrg + tile_base : NULL, m, l, acc);
-    /* finalisation (Alg. 1, steps 20-21) */
+    /* finalisation: O = u / l and LSE = m + log l */
     for (int64_t r = 0; r < nrows; ++r) {
       const int64_t row = (b * p->heads_q + h) * Nq + q0 + r;
       for (int c = 0; c < d; ++c) {
@@ -413,9 +413,9 @@ static void bwd_tile_apply(const orc_problem* p, const double* q, const double* 
       if (!legal(p, qi, kj)) continue;
       const int64_t krow = (b * p->heads_kv + g) * Nk + kj;
       const double sv = p->scale * dot(q + row * d, k + krow * d, d);
-      const double pr = exp(sv - lse[row]);                    /* Alg. 2 step 13 */
-      const double dp = dot(dout + row * d, v + krow * d, d);  /* Alg. 2 step 13 */
-      const double ds = pr * (dp - D[row]);                    /* Alg. 2 step 14 */
+      const double pr = exp(sv - lse[row]);                    /* P from the saved LSE */
+      const double dp = dot(dout + row * d, v + krow * d, d);  /* dP = dO . v */
+      const double ds = pr * (dp - D[row]);                    /* dS = P (dP - D) */
       const double pu = (p->round_flags & ORC_ROUND_P_BWD) ? round_bf16(pr) : pr;
       double du = (p->round_flags & ORC_ROUND_DS) ? round_bf16(ds) : ds;
       const int dsens = (p->round_flags & ORC_ABS_D) != 0;
@@ -453,7 +453,7 @@ int orc_mala_bwd(const orc_problem* p, const double* q, const double* k, const d
   const int64_t nk = sel_k ? nsel_k : (all ? (int64_t)p->batch * p->heads_kv * Tc : 0);
   const int64_t ntiles = (int64_t)p->batch * p->heads_q * Tr * Tc;
 
-  /* D_q = rowsum(O o dO) from the stored O (Alg. 2 step 14) */
+  /* D_q = rowsum(O o dO) from the stored O (Algorithm 2) */
   const int64_t nrow = (int64_t)p->batch * p->heads_q * Nq;
   double* D = (double*)malloc(sizeof(double) * (size_t)(nrow > 0 ? nrow : 1));
   double* Dabs = (double*)malloc(sizeof(double) * (size_t)(nrow > 0 ? nrow : 1));
