@@ -91,6 +91,7 @@ def _load():
         _lib.orc_mala_decode.argtypes = [pr, dp, dp, dp, ctypes.c_int32, i8, dp, dp, i8, dp]
         _lib.orc_merge.argtypes = [ctypes.c_int32, ctypes.c_int32, dp, dp, dp, dp, dp]
         _lib.orc_round_bf16_array.argtypes = [dp, dp, ctypes.c_int64]
+        _lib.orc_num_threads.argtypes = []
     return _lib
 
 
@@ -251,6 +252,11 @@ def merge(m, l, u):
                       _ptr(np.ascontiguousarray(u), ctypes.c_double), _ptr(o, ctypes.c_double),
                       _ptr(z, ctypes.c_double))
     return o, float(z[0])
+
+
+def num_threads():
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().orc_num_threads())
 
 
 def round_bf16(x):

@@ -40,6 +40,9 @@
  * product operand, and rounds outputs to bf16. Everything else stays fp64.
  */
 #include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -632,6 +635,16 @@ int orc_mala_decode(const orc_problem* p, const double* q, const double* k, cons
 }
 
 /* bf16 rounding exposed for the tests' own rounding of inputs/expectations */
+/* Number of OpenMP threads the parallel loops above use (reported with the
+ * oracle's timings). */
+int orc_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
 void orc_round_bf16_array(const double* x, double* y, int64_t n) {
   for (int64_t i = 0; i < n; ++i) y[i] = round_bf16(x[i]);
 }
