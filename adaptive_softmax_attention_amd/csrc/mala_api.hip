@@ -113,7 +113,14 @@ int bwd_common(const mala_shape* shape, const mala_config* cfg, const void* q, c
   const size_t need = mala_bwd_workspace_bytes(shape, cfg);
   if (!workspace || workspace_bytes < need) return MALA_ERR_WORKSPACE;
   const int64_t tc = (shape->seqlen_k + 63) / 64;
+  const int64_t tr = (shape->seqlen_q + 63) / 64;
   if ((int64_t)shape->batch * shape->heads_kv * tc > kMaxGrid) return MALA_ERR_UNSUPPORTED;
+  if ((int64_t)shape->batch * shape->heads_q * ((tr + 3) / 4 + 1) > kMaxGrid)
+    return MALA_ERR_UNSUPPORTED;
+  // row-term pass: one 256-thread group per 16 (d = 64) or 8 (d = 128) padded rows
+  if ((int64_t)shape->batch * shape->heads_q * tr * 64 * (shape->head_dim / 8) / 256 + 1 >
+      kMaxGrid)
+    return MALA_ERR_UNSUPPORTED;
   st = check_device();
   if (st) return st;
   mala::BwdArgs a;
@@ -126,9 +133,7 @@ int bwd_common(const mala_shape* shape, const mala_config* cfg, const void* q, c
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  const size_t rows = (size_t)shape->batch * shape->heads_q * shape->seqlen_q;
-  a.delta = (float*)workspace;
-  a.dq_accum = (float*)((char*)workspace + align256(rows * sizeof(float)));
+  a.workspace = workspace;
   a.batch = shape->batch;
   a.heads_q = shape->heads_q;
   a.heads_kv = shape->heads_kv;
@@ -201,8 +206,8 @@ int fullattn_fwd(const mala_shape* shape, const mala_config* cfg, const void* q,
 
 size_t mala_bwd_workspace_bytes(const mala_shape* shape, const mala_config* cfg) {
   if (check_shape(shape) || check_config(cfg, false)) return 0;
-  const size_t rows = (size_t)shape->batch * shape->heads_q * shape->seqlen_q;
-  return align256(rows * sizeof(float)) + align256(rows * shape->head_dim * sizeof(float));
+  return mala::bwd_workspace_bytes(shape->batch, shape->heads_q, shape->seqlen_q,
+                                   shape->seqlen_k, cfg->causal);
 }
 
 int mala_bwd(const mala_shape* shape, const mala_config* cfg, const void* q, const void* k,

@@ -1,36 +1,51 @@
 // MALA fused backward ("MassAlloc Attention: Let Attention Allocate Its Own Compute":
 // Sec. 2.2 Eq. 4, Appendix A Algorithm 2, and the backward part of
-// Appendix A.1) and the dense FullAttn backward
-// from the same template with the test compiled out.
+// Appendix A.1) and the dense FullAttn backward from the same templates with
+// the test compiled out.
 //
-// Three kernels on the caller's stream:
-//   1. bwd_pre:  D_q = rowsum(O o dO) in fp32 (from the
-//                stored O) and a zero fill of the fp32 dQ accumulator (a fill
-//                kernel rather than a memset, so the sequence can be captured
-//                in a graph);
-//   2. bwd_main: key-major traversal. A workgroup of 8 wave64s owns a pair of
-//                64-key blocks (j0 = 2J, j1 = 2J + 1) of one KV head; each wave
-//                owns a 16-key slice and keeps its dK, dV accumulators in
-//                registers. It visits the G query heads of the group and the
-//                query blocks from the diagonal up. Per tile:
-//                S = Q K^T is recomputed (16x16x32 bf16 MFMA), the offline test
-//                of Eq. 4 compares every legal s - z_q with log(tau/L_q) against
-//                the forward's LSE (wave ballot, OR over the block's 4 waves at
-//                the barrier that precedes the dO load); only a retained tile
-//                loads dO and runs P = exp(s - z), dP = dO V^T,
-//                dS = P o (dP - D), dV += P^T dO, dK += dS^T Q and
-//                dQ += dS K. P and dS come out of the score MFMA already in the
-//                A-operand layout of the dV / dK products; dS goes through LDS
-//                so dQ contracts over both key blocks (128 keys) before the
-//                fp32 atomic add into the accumulator;
-//   3. bwd_dq:   dQ = bf16(scale * accumulator).
-// Q and dO tiles are staged in LDS twice, row-major for the products that
-// contract over d and transposed for those that contract over queries.
+// The offline test of Eq. 4 compares every legal score with the forward's
+// final log-normaliser, so a tile's decision does not depend on the order in
+// which tiles are visited and can be shared between passes. Three kernels on
+// the caller's stream:
+//   1. bwd_pre: per query row, D = rowsum(O o dO) in fp32 from the stored
+//      O, z2 = LSE * log2(e), and the test folded into one raw-score
+//      threshold W = (z2 + log2(tau / L_q)) / (scale * log2(e)): a legal
+//      entry keeps its tile iff s >= W. Written per 64-row block as
+//      [z2 x64][W x64][D x64][unused x64] (padded rows: z2 = W = +inf, so
+//      they neither pass the test nor contribute, P = 0).
+//   2. bwd_kv: key-major. A workgroup of 4 wave64s (one per SIMD, so each
+//      wave may hold up to 512 registers) owns 128 keys: key blocks 2J and
+//      2J + 1 of one KV head, two waves per block. Each wave holds its 32
+//      keys of K as MFMA B operands (S = Q K^T) and their dK, dV
+//      accumulators; V of the 128 keys sits in LDS. It visits (query block, query head) items from
+//      the last query block down to the diagonal, so the workgroups running
+//      at the same time read the same Q tiles (L2 reuse within an XCD).
+//      Per item: S is recomputed (16x16x32 bf16 MFMA), the test is one
+//      compare per score, a ballot per block and an OR over the 4 waves at
+//      a barrier. The decision goes to a byte map in the workspace. Only a
+//      kept tile requests dO; its post-score work (P, dP, dS, dV += P^T dO,
+//      dK += dS^T Q) runs one item later, so dO arrives while the next item
+//      is scored. Q (with the row terms) and dO are copied asynchronously
+//      from global memory into LDS rings; waves 0-1 issue the Q copies and
+//      waves 2-3 the dO copies, so each wave's in-order memory counter
+//      tracks a single stream. The transposed operands (dO and Q with the
+//      query index as reduction index) come from the transposing LDS read
+//      of the same tiles.
+//   3. bwd_dq: query-major, shaped like the forward (a wave pair per 64-row
+//      block, 4 blocks per workgroup sharing K/V tiles). It reads the byte
+//      map, lists the key blocks that some block of the workgroup keeps,
+//      and for those recomputes S^T = K Q^T and dP^T = V dO^T, forms
+//      dS^T and accumulates dQ^T += K^T dS^T in registers: dQ is written
+//      once, in bf16, with no atomics and no fp32 accumulator in memory.
+#include <type_traits>
+
 #include "mala_common.h"
 #include "mala_internal.h"
 
 namespace mala {
 namespace {
+
+constexpr int kRowInfo = 256;  // floats of row terms per 64-row block
 
 struct BwdParams {
   const __bf16* q;
@@ -42,420 +57,664 @@ struct BwdParams {
   __bf16* dq;
   __bf16* dk;
   __bf16* dv;
-  float* delta;
-  float* dq_accum;
+  float* rowinfo;  // [B*Hq*Tr][kRowInfo]
+  uint8_t* dmap;   // backward decisions, see dmap_index()
   int batch, heads_q, heads_kv, nq, nk, group;
   int causal;
   float scale;
-  float c;         // scale * log2(e)
+  float c;         // scale * log2(e): raw score -> log2 units
   float log2_tau;  // log2(tau); -inf for tau = 0, +inf for tau = inf
   int tr, tc, npair;
+  long long dmap_per_head;   // bytes of the decision map per (batch, query head)
+  int hpw, ipw, n_hg, n_ig;  // query-major grid (as the forward)
   unsigned long long* counters;
   uint8_t* decisions;
 };
+
+// Decision byte of tile (i, j) of (batch, query head) bh: causal problems
+// store only the lower triangle.
+__device__ __forceinline__ long long dmap_index(const BwdParams& p, int bh, int i, int j) {
+  const long long t = p.causal ? (long long)i * (i + 1) / 2 + j : (long long)i * p.tc + j;
+  return (long long)bh * p.dmap_per_head + t;
+}
+
+// MFMA row R of subtile x holds row 32(x/2) + 8(R/4) + 4(x%2) + R%4 of the
+// 64-row tile, so output lane group g4 holds the 8 consecutive rows
+// 32(x/2) + 8 g4 + 0..7 across the subtile pair (2kc, 2kc + 1): the outputs
+// are then already a reduction-side MFMA operand over those rows.
+__device__ __forceinline__ int qperm(int x, int R) {
+  return 32 * (x >> 1) + 8 * (R >> 2) + 4 * (x & 1) + (R & 3);
+}
 
 // ---------------------------------------------------------------- pre ----
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
   constexpr int LPR = D / 8;  // lanes per row (8 values each)
-  const long long rows = (long long)p.batch * p.heads_q * p.nq;
+  const long long nprow = (long long)p.batch * p.heads_q * p.tr * 64;
   const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
-  const long long row = t / LPR;
+  const long long prow = t / LPR;  // row index padded to whole blocks
   const int part = (int)(t % LPR);
+  const long long blk = prow / 64;
+  const int r = (int)(prow % 64);
+  const long long bh = blk / p.tr;
+  const int i = (int)(blk % p.tr);
+  const int qq = 64 * i + r;
+  const bool valid = prow < nprow && qq < p.nq;
+  const long long row = bh * p.nq + qq;
   float acc = 0.f;
-  if (row < rows) {
+  if (valid) {
     const bf16x8 a = *(const bf16x8*)(p.o + row * D + 8 * part);
     const bf16x8 b = *(const bf16x8*)(p.dout + row * D + 8 * part);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc += (float)a[e] * (float)b[e];
-    float* z = p.dq_accum + row * D + 8 * part;
-    *(float4*)z = make_float4(0.f, 0.f, 0.f, 0.f);
-    *(float4*)(z + 4) = make_float4(0.f, 0.f, 0.f, 0.f);
   }
 #pragma unroll
   for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && part == 0) p.delta[row] = acc;
+  if (prow < nprow && part == 0) {
+    float* ri = p.rowinfo + blk * kRowInfo;
+    if (valid) {
+      const float z2 = p.lse[row] * kLog2e;
+      const float L = p.causal ? (float)(qq + 1) : (float)p.nk;  // visible keys
+      ri[r] = z2;
+      ri[64 + r] = (z2 + p.log2_tau - log2f(L)) / p.c;
+      ri[128 + r] = acc;
+    } else {
+      ri[r] = INFINITY;
+      ri[64 + r] = INFINITY;
+      ri[128 + r] = 0.f;
+    }
+  }
 }
 
-// ---------------------------------------------------------------- dq -----
-template <int D>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
-  const long long n = (long long)p.batch * p.heads_q * p.nq * D / 8;
-  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (t >= n) return;
-  const float4 a = *(const float4*)(p.dq_accum + 8 * t);
-  const float4 b = *(const float4*)(p.dq_accum + 8 * t + 4);
-  bf16x8 r;
-  r[0] = to_bf16(a.x * p.scale);
-  r[1] = to_bf16(a.y * p.scale);
-  r[2] = to_bf16(a.z * p.scale);
-  r[3] = to_bf16(a.w * p.scale);
-  r[4] = to_bf16(b.x * p.scale);
-  r[5] = to_bf16(b.y * p.scale);
-  r[6] = to_bf16(b.z * p.scale);
-  r[7] = to_bf16(b.w * p.scale);
-  *(bf16x8*)(p.dq + 8 * t) = r;
-}
+// ----------------------------------------------------------------- kv ----
+template <int D, bool kTest, bool kStats>
+__global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
+  constexpr int NDC = D / 32;           // reduction chunks over d
+  constexpr int NDS = D / 16;           // 16-column subtiles of d
+  constexpr int KCH = D / 8;            // 16-byte chunks per row
+  constexpr int QCPT = 64 * KCH / 128;  // copies per lane per tile (2 waves copy)
+  constexpr int RQ = 4;                 // Q ring: current, deferred, 2 ahead
+  constexpr int PF = 2;                 // Q prefetch distance (items)
 
-// --------------------------------------------------------------- main ----
-// LDS layouts (bf16): row-major tiles use 16-byte chunks XOR-swizzled by
-// k_swz(row); transposed tiles [d][rows] use v_swz(d) on 128-byte rows, and
-// the 256-byte-row tiles (K^T over 128 keys, dS over 128 keys) use ds_swz.
-__device__ __forceinline__ int ds_swz(int row) { return (row & 7) ^ ((row >> 3) & 7); }
+  __shared__ __attribute__((aligned(16))) __bf16 q_ring[RQ][64 * D];
+  __shared__ __attribute__((aligned(16))) float ri_ring[RQ][kRowInfo];
+  __shared__ __attribute__((aligned(16))) __bf16 do_ring[2][64 * D];
+  __shared__ __attribute__((aligned(16))) __bf16 v_lds[128 * D];  // V of the 128 keys
+  __shared__ int flags[4];
 
-template <int D, bool kTest>
-__global__ __launch_bounds__(512, 1) void bwd_main_kernel(BwdParams p) {
-  constexpr int NT = 512;
-  constexpr int NDC = D / 32;       // reduction chunks over d
-  constexpr int NDS = D / 16;       // 16-column subtiles of d
-  constexpr int KCH = D / 8;        // 16-byte chunks per row of d
-  constexpr int QPT = 64 * KCH / NT;   // Q / dO rows staged per thread (2 or 1)
-  constexpr int KTPT = 128 * KCH / NT;  // K rows staged per thread for K^T (4 or 2)
-  constexpr int DQS = NDS / 2;      // d subtiles per wave in the dQ product
-
-  __shared__ __attribute__((aligned(16))) __bf16 q_lds[64 * D];
-  __shared__ __attribute__((aligned(16))) __bf16 qt_lds[D * 64];
-  __shared__ __attribute__((aligned(16))) __bf16 do_lds[64 * D];
-  __shared__ __attribute__((aligned(16))) __bf16 dot_lds[D * 64];
-  __shared__ __attribute__((aligned(16))) __bf16 kt_lds[D * 128];
-  __shared__ __attribute__((aligned(16))) __bf16 ds_lds[64 * 128];
-  __shared__ __attribute__((aligned(16))) float z_lds[64];
-  __shared__ __attribute__((aligned(16))) float t_lds[64];
-  __shared__ __attribute__((aligned(16))) float d_lds[64];
-  __shared__ int flags[8];
-
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l16 = lane & 15, g4 = lane >> 4;
-  const int kb = w >> 2, kw = w & 3;
 
-  // ---- work item: key-block pair J of (b, kvh), longest first ----
+  // ---- work item: key blocks (2J, 2J + 1) of (b, kvh), longest first ----
   const int per = p.batch * p.heads_kv;
   const int J = (int)(blockIdx.x / per);
   const int bk = (int)(blockIdx.x % per);
   const int b = bk / p.heads_kv, kvh = bk % p.heads_kv;
   const int j0 = 2 * J;
-  const int jw = j0 + kb;                 // this wave's key block
-  const int key = 64 * jw + 16 * kw + l16;  // this lane's key (score column)
-  const bool kb_valid = jw < p.tc;
+  const bool has1 = j0 + 1 < p.tc;  // the second key block exists
+  const int kb = w >> 1;            // this wave's key block: 2J + kb
+  const int jw = j0 + kb;
   const __bf16* kbase = p.k + (size_t)bk * p.nk * D;
   const __bf16* vbase = p.v + (size_t)bk * p.nk * D;
 
-  // K and V of this lane's key as B operands (fixed for the workgroup)
-  bf16x8 kreg[NDC], vreg[NDC];
+  // K of this wave's 32 keys (two 16-key subtiles) as B operands in
+  // registers; V of the workgroup's 128 keys in LDS (read by kept items
+  // only), 16-byte chunks XOR-swizzled by the key row so that 16
+  // consecutive rows of one chunk hit distinct banks
+  int key[2];
+  bf16x8 kreg[2][NDC];
 #pragma unroll
-  for (int dc = 0; dc < NDC; ++dc) {
-    const bool ok = key < p.nk;
-    kreg[dc] = ok ? *(const bf16x8*)(kbase + (size_t)key * D + 32 * dc + 8 * g4) : bf16x8{};
-    vreg[dc] = ok ? *(const bf16x8*)(vbase + (size_t)key * D + 32 * dc + 8 * g4) : bf16x8{};
+  for (int ns = 0; ns < 2; ++ns) {
+    key[ns] = 64 * jw + 32 * (w & 1) + 16 * ns + l16;
+    const bool ok = key[ns] < p.nk;
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc)
+      kreg[ns][dc] =
+          ok ? *(const bf16x8*)(kbase + (size_t)key[ns] * D + 32 * dc + 8 * g4) : bf16x8{};
   }
-  // K^T of both key blocks into LDS for the dQ product
-  {
-    const int ch = tid % KCH, kg = tid / KCH;
-    bf16x8 kr[KTPT];
 #pragma unroll
-    for (int x = 0; x < KTPT; ++x) {
-      const int kk = 64 * j0 + kg * KTPT + x;
-      kr[x] = kk < p.nk ? *(const bf16x8*)(kbase + (size_t)kk * D + 8 * ch) : bf16x8{};
+  for (int x = 0; x < 128 * KCH / 256; ++x) {
+    const int c = x * 256 + tid;
+    const int row = c / KCH, ch = c % KCH;
+    const int kk = 64 * j0 + row;
+    const bf16x8 val = kk < p.nk ? *(const bf16x8*)(vbase + (size_t)kk * D + 8 * ch) : bf16x8{};
+    *(bf16x8*)(v_lds + row * D + ((ch ^ row) & (KCH - 1)) * 8) = val;
+  }
+  // (the first barrier of the item loop orders these stores before any read)
+
+  floatx4 dk_acc[2][NDS], dv_acc[2][NDS];
+#pragma unroll
+  for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      dk_acc[ns][ds] = floatx4{0.f, 0.f, 0.f, 0.f};
+      dv_acc[ns][ds] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
+
+  // items: query blocks from the last one down to the first with a legal
+  // entry for key block 2J, query heads of the group innermost
+  const int i_lo = p.causal ? j0 : 0;
+  const int n_items = p.group * (p.tr - i_lo);
+  auto item_i = [&](int it) { return p.tr - 1 - it / p.group; };
+  auto item_h = [&](int it) { return kvh * p.group + it % p.group; };
+
+  // ---- async copies of a 64-row tile (rows past the end re-read the last
+  //      row: their row terms make them inert) ----
+  auto issue_rows = [&](const __bf16* src, int i, __bf16* slot, int cw) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = 8 * ch + e;
-      const int k0 = kg * KTPT;
-      __bf16* dst = kt_lds + d * 128 + (((k0 >> 3) ^ (d & 15)) * 8) + (k0 & 7);
-      if constexpr (KTPT == 4) {
-        bf16x4 t4;
-        t4[0] = kr[0][e];
-        t4[1] = kr[1][e];
-        t4[2] = kr[2][e];
-        t4[3] = kr[3][e];
-        *(bf16x4*)dst = t4;
-      } else {
-        typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
-        bf16x2 t2;
-        t2[0] = kr[0][e];
-        t2[1] = kr[1][e];
-        *(bf16x2*)dst = t2;
+    for (int x = 0; x < QCPT; ++x) {
+      const int s0 = (2 * x + cw) * 64;  // first 16-byte chunk of this copy
+      const int s = s0 + lane;
+      const int row = s / KCH, pc = s % KCH;
+      const int qq = min(64 * i + row, p.nq - 1);
+      async_copy16(src + (size_t)qq * D + ((pc ^ dsw(row)) & (KCH - 1)) * 8, slot + s0 * 8);
+    }
+  };
+  auto issue_q = [&](int it) {  // waves 0 and 1
+    const int i = item_i(it), h = item_h(it), slot = it % RQ;
+    issue_rows(p.q + (size_t)(b * p.heads_q + h) * p.nq * D, i, q_ring[slot], w);
+    if (w == 0)
+      async_copy16(p.rowinfo + ((size_t)(b * p.heads_q + h) * p.tr + i) * kRowInfo + 4 * lane,
+                   ri_ring[slot]);
+  };
+  auto issue_do = [&](int it) {  // waves 2 and 3
+    const int i = item_i(it), h = item_h(it);
+    issue_rows(p.dout + (size_t)(b * p.heads_q + h) * p.nq * D, i, do_ring[it & 1], w - 2);
+  };
+  // memory operations of waves 0 / 1 per item: the Q copy (+ the row terms
+  // on wave 0) and, on wave 0, one decision store
+  const int cq = QCPT + (w == 0 ? 1 : 0);
+
+  // A operand: rows qperm(qs, l16) of a row-major tile, reduction chunk dc
+  auto a_rows = [&](const __bf16* t, int qs, int dc) {
+    const int row = qperm(qs, l16);
+    const int ch = 4 * dc + g4;
+    return *(const bf16x8*)(t + row * D + ((ch ^ dsw(row)) & (KCH - 1)) * 8);
+  };
+  // B operand: column 16 ds + l16 of a row-major tile over the 8 rows
+  // 32 kc + 8 g4 + 0..7, from two transposing reads
+  auto b_cols = [&](const __bf16* t, int kc, int ds) {
+    short4v h2[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int row = 32 * kc + 8 * g4 + 4 * hh + (l16 >> 2);
+      const int col = 16 * ds + 4 * (l16 & 3);
+      h2[hh] = lds_read_tr4(t + row * D + (((col >> 3) ^ dsw(row)) & (KCH - 1)) * 8 + (col & 7));
+    }
+    return join_tr(h2[0], h2[1]);
+  };
+
+  // post-score work of a kept item, one half of the 64 queries (query
+  // subtiles 2kc, 2kc + 1) at a time
+  auto post = [&](int itp, const floatx4(&sp)[4][2]) {
+    const __bf16* qt = q_ring[itp % RQ];
+    const __bf16* dt = do_ring[itp & 1];
+    const float* ri = ri_ring[itp % RQ];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      // dP = dO V^T for query subtiles 2kc, 2kc + 1 (same layout as S)
+      floatx4 dp[2][2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        dp[x][0] = floatx4{0.f, 0.f, 0.f, 0.f};
+        dp[x][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc) {
+        bf16x8 bv[2];
+#pragma unroll
+        for (int ns = 0; ns < 2; ++ns) {
+          const int row = 64 * kb + 32 * (w & 1) + 16 * ns + l16;
+          const int ch = 4 * dc + g4;
+          bv[ns] = *(const bf16x8*)(v_lds + row * D + ((ch ^ row) & (KCH - 1)) * 8);
+        }
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const bf16x8 a = a_rows(dt, 2 * kc + x, dc);
+          dp[x][0] = mfma16x16x32(a, bv[0], dp[x][0]);
+          dp[x][1] = mfma16x16x32(a, bv[1], dp[x][1]);
+        }
+      }
+      // P = exp2(s c - z2), dS = P (dP - D), packed as A operands [key][query]
+      bf16x8 pa[2], da[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int qs = 2 * kc + x;
+        const int ql = 32 * kc + 8 * g4 + 4 * x;
+        const float4 z4 = *(const float4*)(ri + ql);
+        const float4 d4 = *(const float4*)(ri + 128 + ql);
+        const float zz[4] = {z4.x, z4.y, z4.z, z4.w};
+        const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float pv = fast_exp2(sp[qs][ns][r] * p.c - zz[r]);
+            const float dsv = pv * (dp[x][ns][r] - dd[r]);
+            pa[ns][4 * x + r] = to_bf16(pv);
+            da[ns][4 * x + r] = to_bf16(dsv);
+          }
+      }
+      // dV += P^T dO, dK += dS^T Q over these 32 queries
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        const bf16x8 bo = b_cols(dt, kc, ds);
+        const bf16x8 bq = b_cols(qt, kc, ds);
+#pragma unroll
+        for (int ns = 0; ns < 2; ++ns) {
+          dv_acc[ns][ds] = mfma16x16x32(pa[ns], bo, dv_acc[ns][ds]);
+          dk_acc[ns][ds] = mfma16x16x32(da[ns], bq, dk_acc[ns][ds]);
+        }
       }
     }
+  };
+
+  // ---- software pipeline over the items ----
+  if (w < 2 && n_items > 0) {
+    issue_q(0);
+    if (n_items > 1) issue_q(1);
   }
-
-  floatx4 dk_acc[NDS], dv_acc[NDS];
+  bool pend = false;  // some block kept the previous item (its dO was requested)
+  bool pret = false;  // this wave's block kept the previous item
+  floatx4 sp[4][2];   // previous item's scores
 #pragma unroll
-  for (int ds = 0; ds < NDS; ++ds) {
-    dk_acc[ds] = floatx4{0.f, 0.f, 0.f, 0.f};
-    dv_acc[ds] = floatx4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  // ---- Q / dO staging: thread owns QPT rows x 8 columns of d ----
-  const int sch = tid % KCH, sg = tid / KCH;  // column chunk, row group
-  auto load_rows = [&](const __bf16* base, int i, bf16x8 (&r)[QPT]) {
-#pragma unroll
-    for (int x = 0; x < QPT; ++x) {
-      const int qq = 64 * i + sg * QPT + x;
-      r[x] = qq < p.nq ? *(const bf16x8*)(base + (size_t)qq * D + 8 * sch) : bf16x8{};
-    }
-  };
-  auto store_rows = [&](const bf16x8 (&r)[QPT], __bf16* nat, __bf16* tr) {
-#pragma unroll
-    for (int x = 0; x < QPT; ++x) {
-      const int row = sg * QPT + x;
-      *(bf16x8*)(nat + row * D + ((sch ^ (k_swz(row) & (KCH - 1))) * 8)) = r[x];
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = 8 * sch + e;
-      const int r0 = sg * QPT;
-      __bf16* dst = tr + d * 64 + (((r0 >> 3) ^ v_swz(d)) * 8) + (r0 & 7);
-      if constexpr (QPT == 2) {
-        typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
-        bf16x2 t2;
-        t2[0] = r[0][e];
-        t2[1] = r[1][e];
-        *(bf16x2*)dst = t2;
-      } else {
-        *dst = r[0][e];
-      }
-    }
-  };
-
-  const int i_first = p.causal ? j0 : 0;
-  const int n_i = p.tr - i_first;
-  const int n_items = n_i > 0 ? p.group * n_i : 0;
-  // Q rows and the LSE of the next item are prefetched into registers one
-  // item ahead (the LDS-only barriers leave those loads in flight)
-  bf16x8 qreg[QPT];
-  float lreg = 0.f;
-  auto load_lse = [&](int h, int i) {
-    const int qq = 64 * i + tid;
-    lreg = (tid < 64 && qq < p.nq) ? p.lse[(size_t)(b * p.heads_q + h) * p.nq + qq] : 0.f;
-  };
-  if (n_items > 0) {
-    const int h = kvh * p.group;
-    load_rows(p.q + (size_t)(b * p.heads_q + h) * p.nq * D, i_first, qreg);
-    load_lse(h, i_first);
+  for (int qs = 0; qs < 4; ++qs) {
+    sp[qs][0] = floatx4{0.f, 0.f, 0.f, 0.f};
+    sp[qs][1] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
   for (int it = 0; it < n_items; ++it) {
-    const int hh = it / n_i;
-    const int i = i_first + it % n_i;
-    const int h = kvh * p.group + hh;
-    const size_t row0 = (size_t)(b * p.heads_q + h) * p.nq;
-
-    lds_barrier();  // previous item's LDS reads complete
-    store_rows(qreg, q_lds, qt_lds);
-    if (tid < 64) {
-      const int qq = 64 * i + tid;
-      z_lds[tid] = lreg * kLog2e;
-      const float L = p.causal ? (float)(qq + 1) : (float)p.nk;
-      t_lds[tid] = p.log2_tau - log2f(L);  // log2(tau / L_q)
+    const int i = item_i(it), h = item_h(it);
+    // Q(it) complete on the copying waves. Issued after it: Q(it + 1) and,
+    // on wave 0, the decision stores of the two previous items.
+    if (kStats) {
+      vmcnt_wait<0>();
+    } else if (w < 2) {
+      vmcnt_wait_le((it + 1 < n_items ? cq : 0) + (w == 0 ? min(it, 2) : 0));
     }
-    lds_barrier();  // Q_i, z, thresholds visible
-    if (it + 1 < n_items) {
-      const int hn = kvh * p.group + (it + 1) / n_i;
-      const int in = i_first + (it + 1) % n_i;
-      load_rows(p.q + (size_t)(b * p.heads_q + hn) * p.nq * D, in, qreg);
-      load_lse(hn, in);
-    }
+    lds_barrier();  // Q(it) visible; every wave is done with item it - 1
+    if (w < 2 && it + PF < n_items) issue_q(it + PF);
 
-    const bool part = kb_valid && (!p.causal || i >= jw);
+    const __bf16* qt = q_ring[it % RQ];
+    const float* ri = ri_ring[it % RQ];
+    // block 2J has a legal entry for every item; block 2J + 1 from i > 2J on
+    const bool part1 = has1 && (!p.causal || i > j0);
+    const bool part = kb == 0 || part1;
+    floatx4 s[4][2];
+#pragma unroll
+    for (int qs = 0; qs < 4; ++qs) {
+      s[qs][0] = floatx4{0.f, 0.f, 0.f, 0.f};
+      s[qs][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
     bool want = false;
-    floatx4 s[4];
     if (part) {
-      // S = Q_i K_j^T recomputed; MFMA row R of query
-      // subtile qs holds query 32(qs/2) + 8(R/4) + 4(qs%2) + R%4
 #pragma unroll
-      for (int qs = 0; qs < 4; ++qs) s[qs] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int dc = 0; dc < NDC; ++dc) {
+      for (int dc = 0; dc < NDC; ++dc)
 #pragma unroll
         for (int qs = 0; qs < 4; ++qs) {
-          const int qr = 32 * (qs >> 1) + 8 * (l16 >> 2) + 4 * (qs & 1) + (l16 & 3);
-          const int ch = 4 * dc + g4;
-          const bf16x8 a = *(const bf16x8*)(q_lds + qr * D + ((ch ^ (k_swz(qr) & (KCH - 1))) * 8));
-          s[qs] = mfma16x16x32(a, kreg[dc], s[qs]);
+          const bf16x8 a = a_rows(qt, qs, dc);
+          s[qs][0] = mfma16x16x32(a, kreg[0][dc], s[qs][0]);
+          s[qs][1] = mfma16x16x32(a, kreg[1][dc], s[qs][1]);
         }
+      // causal mask at the diagonal and the ragged key tail
+      const bool need_mask = (p.causal && i == jw) || (64 * jw + 64 > p.nk);
+      if (need_mask) {
+#pragma unroll
+        for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+          for (int qs = 0; qs < 4; ++qs)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int qq = 64 * i + qperm(qs, 4 * g4 + r);
+              if (key[ns] >= p.nk || (p.causal && key[ns] > qq)) s[qs][ns][r] = -INFINITY;
+            }
       }
-      // legality and the offline test of Eq. 4 (log2 units)
+      if constexpr (kTest) {
+        // Eq. 4: keep iff some legal entry has s >= W_q (masked entries are
+        // -inf; W_q = -inf only for tau = 0, where every legal tile is kept)
+        bool wt = false;
 #pragma unroll
-      for (int qs = 0; qs < 4; ++qs) {
-        const int ql = 32 * (qs >> 1) + 8 * g4 + 4 * (qs & 1);  // first of 4 queries
-        const float4 z4 = *(const float4*)(z_lds + ql);
-        const float4 t4 = *(const float4*)(t_lds + ql);
-        const float zz[4] = {z4.x, z4.y, z4.z, z4.w};
-        const float tt[4] = {t4.x, t4.y, t4.z, t4.w};
+        for (int qs = 0; qs < 4; ++qs) {
+          const float4 w4 = *(const float4*)(ri + 64 + 32 * (qs >> 1) + 8 * g4 + 4 * (qs & 1));
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int qq = 64 * i + ql + r;
-          const bool legal = qq < p.nq && key < p.nk && (!p.causal || key <= qq);
-          const float x = s[qs][r] * p.c - zz[r];  // log2 P
-          s[qs][r] = legal ? x : -INFINITY;
-          if constexpr (kTest) {
-            if (legal && !(x < tt[r])) want = true;
-          } else {
-            if (legal) want = true;
+          for (int ns = 0; ns < 2; ++ns) {
+            wt |= s[qs][ns][0] >= w4.x;
+            wt |= s[qs][ns][1] >= w4.y;
+            wt |= s[qs][ns][2] >= w4.z;
+            wt |= s[qs][ns][3] >= w4.w;
           }
         }
+        want = wave_any(wt);
+      } else {
+        want = true;
       }
-      want = wave_any(want);
     }
     if (lane == 0) flags[w] = want ? 1 : 0;
-    lds_barrier();
-    const bool ret0 = (flags[0] | flags[1] | flags[2] | flags[3]) != 0;
-    const bool ret1 = (flags[4] | flags[5] | flags[6] | flags[7]) != 0;
-    const bool retain = part && (kb == 0 ? ret0 : ret1);
-    if (kw == 0 && lane == 0 && part) {
-      if (p.counters) {
-        atomicAdd(&p.counters[0], 1ull);
-        if (retain) {
-          atomicAdd(&p.counters[1], 1ull);
-          atomicAdd(&p.counters[2], (unsigned long long)min(64, p.nq - 64 * i) * 64ull);
-        }
-      }
-      if (p.decisions)
-        p.decisions[((size_t)(b * p.heads_q + h) * p.tr + i) * p.tc + jw] = retain ? 1 : 0;
+    // dO of the previous item complete (the copying waves' only stream)
+    if (kStats) {
+      vmcnt_wait<0>();
+    } else if (w >= 2 && pend) {
+      vmcnt_wait<0>();
     }
-    if (!ret0 && !ret1) continue;  // both tiles skipped: dO never loaded
+    lds_barrier();  // flags visible; dO(it - 1) visible
+    const bool ret0 = (flags[0] | flags[1]) != 0;
+    const bool ret1 = part1 && (flags[2] | flags[3]) != 0;
+    const bool ret = kb == 0 ? ret0 : ret1;
+    const int bh = b * p.heads_q + h;
+    if (w == 0 && lane < 2) {
+      // lane 0 always stores (block 2J is legal for every item)
+      const bool legal = lane == 0 || part1;
+      const bool r = lane == 0 ? ret0 : ret1;
+      if (legal) p.dmap[dmap_index(p, bh, i, j0 + lane)] = r ? 1 : 0;
+      if (kStats && legal) {
+        if (p.counters) {
+          atomicAdd(&p.counters[0], 1ull);
+          if (r) {
+            atomicAdd(&p.counters[1], 1ull);
+            atomicAdd(&p.counters[2], (unsigned long long)min(64, p.nq - 64 * i) * 64ull);
+          }
+        }
+        if (p.decisions) p.decisions[((size_t)bh * p.tr + i) * p.tc + j0 + lane] = r ? 1 : 0;
+      }
+    }
+    const bool any = ret0 || ret1;
+    if (w >= 2 && any) issue_do(it);
+    if (kStats && any && tid == 128 && p.counters) atomicAdd(&p.counters[3], 1ull);
 
-    // ---- retained: dO_i and D_i ----
-    bf16x8 doreg[QPT];
-    load_rows(p.dout + row0 * D, i, doreg);
-    if (tid == 0 && p.counters) atomicAdd(&p.counters[3], 1ull);
-    if (tid < 64) {
-      const int qq = 64 * i + tid;
-      d_lds[tid] = qq < p.nq ? p.delta[row0 + qq] : 0.f;
-    }
-    if (retain) {
-#pragma unroll
-      for (int qs = 0; qs < 4; ++qs)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) s[qs][r] = fast_exp2(s[qs][r]);  // P
-    }
-    store_rows(doreg, do_lds, dot_lds);
-    lds_barrier();  // dO_i, dO_i^T, D_i visible
+    // the previous item's post-score work (its dO arrived during this scoring)
+    if (pret) post(it - 1, sp);
 
-    if (retain) {
-      // dP = dO V^T, same layout as S
-      floatx4 dp[4];
+    pend = any;
+    pret = ret;
 #pragma unroll
-      for (int qs = 0; qs < 4; ++qs) dp[qs] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int dc = 0; dc < NDC; ++dc) {
-#pragma unroll
-        for (int qs = 0; qs < 4; ++qs) {
-          const int qr = 32 * (qs >> 1) + 8 * (l16 >> 2) + 4 * (qs & 1) + (l16 & 3);
-          const int ch = 4 * dc + g4;
-          const bf16x8 a = *(const bf16x8*)(do_lds + qr * D + ((ch ^ (k_swz(qr) & (KCH - 1))) * 8));
-          dp[qs] = mfma16x16x32(a, vreg[dc], dp[qs]);
-        }
-      }
-      // dS = P o (dP - D); pack P^T and dS^T as A operands
-      bf16x8 pt[2], dst[2];
-#pragma unroll
-      for (int qs = 0; qs < 4; ++qs) {
-        const int ql = 32 * (qs >> 1) + 8 * g4 + 4 * (qs & 1);
-        const float4 d4 = *(const float4*)(d_lds + ql);
-        const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float pv = s[qs][r];
-          const float dsv = pv * (dp[qs][r] - dd[r]);
-          pt[qs >> 1][4 * (qs & 1) + r] = to_bf16(pv);
-          dst[qs >> 1][4 * (qs & 1) + r] = to_bf16(dsv);
-        }
-      }
-      // dV += P^T dO, dK += dS^T Q
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) {
-          const int d = 16 * ds + l16;
-          const int ch = 4 * kc + g4;
-          const bf16x8 bo = *(const bf16x8*)(dot_lds + d * 64 + ((ch ^ v_swz(d)) * 8));
-          const bf16x8 bq = *(const bf16x8*)(qt_lds + d * 64 + ((ch ^ v_swz(d)) * 8));
-          dv_acc[ds] = mfma16x16x32(pt[kc], bo, dv_acc[ds]);
-          dk_acc[ds] = mfma16x16x32(dst[kc], bq, dk_acc[ds]);
-        }
-      // dS into LDS as [query][128 keys] for the dQ product
-      const int kcol = 64 * kb + 16 * kw + l16;
-#pragma unroll
-      for (int qs = 0; qs < 4; ++qs)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int ql = 32 * (qs >> 1) + 8 * g4 + 4 * (qs & 1) + r;
-          ds_lds[ql * 128 + (((kcol >> 3) ^ ds_swz(ql)) * 8) + (kcol & 7)] =
-              dst[qs >> 1][4 * (qs & 1) + r];
-        }
-    }
-    lds_barrier();  // dS of both key blocks visible
-
-    // dQ_i += dS K over the retained key blocks; wave w
-    // computes queries 16(w%4).. and d columns (D/2)(w/4).. of the tile
-    {
-      const int qsd = w & 3, dh = w >> 2;
-      floatx4 acc[DQS];
-#pragma unroll
-      for (int x = 0; x < DQS; ++x) acc[x] = floatx4{0.f, 0.f, 0.f, 0.f};
-      const int qa = 16 * qsd + l16;
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        if (!((kc < 2) ? ret0 : ret1)) continue;
-        const int ch = 4 * kc + g4;
-        const bf16x8 a = *(const bf16x8*)(ds_lds + qa * 128 + ((ch ^ ds_swz(qa)) * 8));
-#pragma unroll
-        for (int x = 0; x < DQS; ++x) {
-          const int d = (D / 2) * dh + 16 * x + l16;
-          const bf16x8 bkt = *(const bf16x8*)(kt_lds + d * 128 + ((ch ^ (d & 15)) * 8));
-          acc[x] = mfma16x16x32(a, bkt, acc[x]);
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int qq = 64 * i + 16 * qsd + 4 * g4 + r;
-        if (qq >= p.nq) continue;
-        float* dst_row = p.dq_accum + (row0 + qq) * D + (D / 2) * dh + l16;
-#pragma unroll
-        for (int x = 0; x < DQS; ++x) atomicAdd(dst_row + 16 * x, acc[x][r]);
-      }
+    for (int qs = 0; qs < 4; ++qs) {
+      sp[qs][0] = s[qs][0];
+      sp[qs][1] = s[qs][1];
     }
   }
+  // the last item's post-score work
+  if (w >= 2 && pend) vmcnt_wait<0>();
+  lds_barrier();
+  if (pret) post(n_items - 1, sp);
 
-  // ---- dK_j = scale * sum, dV_j; rows = keys 4g4 + r ----
+  // ---- dK = scale * sum, dV; output rows = keys 4 g4 + r of subtile ns ----
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int kk = 64 * jw + 16 * kw + 4 * g4 + r;
-    if (!kb_valid || kk >= p.nk) continue;
-    __bf16* dkr = p.dk + ((size_t)bk * p.nk + kk) * D;
-    __bf16* dvr = p.dv + ((size_t)bk * p.nk + kk) * D;
+  for (int ns = 0; ns < 2; ++ns) {
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
-      dkr[16 * ds + l16] = to_bf16(dk_acc[ds][r] * p.scale);
-      dvr[16 * ds + l16] = to_bf16(dv_acc[ds][r]);
+    for (int r = 0; r < 4; ++r) {
+      const int kk = 64 * jw + 32 * (w & 1) + 16 * ns + 4 * g4 + r;
+      if (jw >= p.tc || kk >= p.nk) continue;
+      __bf16* dkr = p.dk + ((size_t)bk * p.nk + kk) * D;
+      __bf16* dvr = p.dv + ((size_t)bk * p.nk + kk) * D;
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        dkr[16 * ds + l16] = to_bf16(dk_acc[ns][ds][r] * p.scale);
+        dvr[16 * ds + l16] = to_bf16(dv_acc[ns][ds][r]);
+      }
     }
   }
 }
 
+// ----------------------------------------------------------------- dq ----
 template <int D>
-hipError_t launch_all(const BwdParams& p, bool test, hipStream_t stream) {
-  const long long rows = (long long)p.batch * p.heads_q * p.nq;
-  const long long pre_threads = rows * (D / 8);
+__global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
+  constexpr int NDC = D / 32;
+  constexpr int NDS = D / 16;
+  constexpr int KCH = D / 8;
+  constexpr int NT = 512;
+  constexpr int NQS = 2;              // 16-query subtiles per wave (32 rows)
+  constexpr int CPT = 64 * KCH / NT;  // async copies per thread per tile
+  constexpr int RK = 3;               // K and V rings: current + 2 ahead
+  constexpr int LMAX = 2048;          // list entries per segment of key blocks
+
+  __shared__ __attribute__((aligned(16))) __bf16 k_ring[RK][64 * D];
+  __shared__ __attribute__((aligned(16))) __bf16 v_ring[RK][64 * D];
+  __shared__ int list[LMAX];
+  __shared__ int wcount[8];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int l16 = lane & 15, g4 = lane >> 4;
+
+  // ---- work item (longest query-block group first), as the forward ----
+  const int per_ig = p.batch * p.heads_kv * p.n_hg;
+  const int ig = p.n_ig - 1 - (int)(blockIdx.x / per_ig);
+  int rem = (int)(blockIdx.x % per_ig);
+  const int hg = rem % p.n_hg;
+  rem /= p.n_hg;
+  const int kvh = rem % p.heads_kv;
+  const int b = rem / p.heads_kv;
+
+  const int blk = w >> 1, half = w & 1;
+  auto blk_h = [&](int x) { return kvh * p.group + hg * p.hpw + (x % p.hpw); };
+  auto blk_i = [&](int x) { return ig * p.ipw + (x / p.hpw); };
+  const int h = blk_h(blk), i = blk_i(blk);
+  const bool valid = i < p.tr;
+  const int q0 = 64 * i + 32 * half;
+  const int i_top = min(ig * p.ipw + p.ipw - 1, p.tr - 1);
+  const int jtop = p.causal ? i_top : p.tc - 1;
+  const size_t qrow0 = (size_t)(b * p.heads_q + h) * p.nq;
+  const __bf16* kbase = p.k + (size_t)(b * p.heads_kv + kvh) * p.nk * D;
+  const __bf16* vbase = p.v + (size_t)(b * p.heads_kv + kvh) * p.nk * D;
+
+  // Q and dO rows of this wave as B operands; row terms per query column
+  bf16x8 qr[NQS][NDC], dr[NQS][NDC];
+  float z2[NQS], dq_d[NQS];
+  floatx4 acc[NDS][NQS];
+#pragma unroll
+  for (int qs = 0; qs < NQS; ++qs) {
+    const int qq = q0 + 16 * qs + l16;
+    const bool ok = valid && qq < p.nq;
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) {
+      qr[qs][dc] = ok ? *(const bf16x8*)(p.q + (qrow0 + qq) * D + 32 * dc + 8 * g4) : bf16x8{};
+      dr[qs][dc] = ok ? *(const bf16x8*)(p.dout + (qrow0 + qq) * D + 32 * dc + 8 * g4) : bf16x8{};
+    }
+    const float* ri =
+        p.rowinfo + ((size_t)(b * p.heads_q + h) * p.tr + (valid ? i : 0)) * kRowInfo;
+    const int ql = 32 * half + 16 * qs + l16;
+    z2[qs] = valid ? ri[ql] : INFINITY;
+    dq_d[qs] = valid ? ri[128 + ql] : 0.f;
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) acc[ds][qs] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  auto issue_tile = [&](const __bf16* base, int j, __bf16* slot) {
+#pragma unroll
+    for (int x = 0; x < CPT; ++x) {
+      const int s0 = x * NT + w * 64;
+      const int s = s0 + lane;
+      const int row = s / KCH, pc = s % KCH;
+      const int kk = min(j * 64 + row, p.nk - 1);
+      async_copy16(base + (size_t)kk * D + ((pc ^ dsw(row)) & (KCH - 1)) * 8, slot + s0 * 8);
+    }
+  };
+
+  // one kept tile: S^T, dP^T, dS^T, dQ^T += K^T dS^T, one half of the 64
+  // keys (key subtiles 2kc, 2kc + 1) at a time
+  auto process = [&](const __bf16* kt, const __bf16* vt, int j) {
+    const bool need_mask = (p.causal && j == i) || (j * 64 + 64 > p.nk);
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      floatx4 s[2][NQS], dp[2][NQS];
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int qs = 0; qs < NQS; ++qs) {
+          s[x][qs] = floatx4{0.f, 0.f, 0.f, 0.f};
+          dp[x][qs] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc)
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          // MFMA row l16 of key subtile 2kc + x holds key qperm(2kc + x, l16)
+          const int kr = qperm(2 * kc + x, l16);
+          const int ch = 4 * dc + g4;
+          const int off = kr * D + ((ch ^ dsw(kr)) & (KCH - 1)) * 8;
+          const bf16x8 ak = *(const bf16x8*)(kt + off);
+          const bf16x8 av = *(const bf16x8*)(vt + off);
+#pragma unroll
+          for (int qs = 0; qs < NQS; ++qs) {
+            s[x][qs] = mfma16x16x32(ak, qr[qs][dc], s[x][qs]);
+            dp[x][qs] = mfma16x16x32(av, dr[qs][dc], dp[x][qs]);
+          }
+        }
+      if (need_mask) {
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+          for (int qs = 0; qs < NQS; ++qs)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int kk = j * 64 + qperm(2 * kc + x, 4 * g4 + r);
+              const int qq = q0 + 16 * qs + l16;
+              if (kk >= p.nk || (p.causal && kk > qq)) s[x][qs][r] = -INFINITY;
+            }
+      }
+      // dS^T = P^T (dP^T - D) as B operands [key][query]: keys 32kc + 8g4 + e
+      bf16x8 db[NQS];
+#pragma unroll
+      for (int qs = 0; qs < NQS; ++qs)
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float pv = fast_exp2(s[x][qs][r] * p.c - z2[qs]);
+            db[qs][4 * x + r] = to_bf16(pv * (dp[x][qs][r] - dq_d[qs]));
+          }
+      // dQ^T += K^T dS^T: A = K^T from transposing reads of the K tile
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        short4v t2[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int row = 32 * kc + 8 * g4 + 4 * hh + (l16 >> 2);
+          const int col = 16 * ds + 4 * (l16 & 3);
+          t2[hh] =
+              lds_read_tr4(kt + row * D + (((col >> 3) ^ dsw(row)) & (KCH - 1)) * 8 + (col & 7));
+        }
+        const bf16x8 a = join_tr(t2[0], t2[1]);
+#pragma unroll
+        for (int qs = 0; qs < NQS; ++qs) acc[ds][qs] = mfma16x16x32(a, db[qs], acc[ds][qs]);
+      }
+    }
+  };
+
+  // ---- segments of at most LMAX candidate key blocks, from the top ----
+  for (int jseg = jtop; jseg >= 0; jseg -= LMAX) {
+    const int jlo = max(0, jseg - LMAX + 1);
+    lds_barrier();  // the previous segment's list is no longer read
+    // list (descending j) of key blocks some block of the group keeps:
+    // entry = j | (block mask << 24)
+    int base = 0;
+    for (int c0 = 0; c0 <= jseg - jlo; c0 += NT) {
+      const int j = jseg - (c0 + tid);
+      int mask = 0;
+      if (j >= jlo) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int ix = blk_i(x);
+          if (ix >= p.tr || (p.causal && j > ix)) continue;
+          const int bh = b * p.heads_q + blk_h(x);
+          if (p.dmap[dmap_index(p, bh, ix, j)] != 0) mask |= 1 << x;
+        }
+      }
+      const unsigned long long bal = __ballot(mask != 0);
+      const int before = __popcll(bal & ((1ull << lane) - 1ull));
+      if (lane == 0) wcount[w] = __popcll(bal);
+      lds_barrier();
+      int off = base;
+      for (int x = 0; x < w; ++x) off += wcount[x];
+      if (mask != 0) list[off + before] = j | (mask << 24);
+      int tot = 0;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) tot += wcount[x];
+      base += tot;
+      lds_barrier();  // wcount reused; list entries visible
+    }
+    const int n = base;
+
+    // pipeline: K and V of the listed tiles two ahead
+    if (n > 0) {
+      const int ja = list[0] & 0xFFFFFF;
+      issue_tile(kbase, ja, k_ring[0]);
+      issue_tile(vbase, ja, v_ring[0]);
+    }
+    if (n > 1) {
+      const int jb = list[1] & 0xFFFFFF;
+      issue_tile(kbase, jb, k_ring[1]);
+      issue_tile(vbase, jb, v_ring[1]);
+    }
+    for (int t = 0; t < n; ++t) {
+      vmcnt_wait_le(t + 1 < n ? 2 * CPT : 0);  // K, V of tile t + 1 may be in flight
+      lds_barrier();
+      if (t + 2 < n) {
+        const int jn = list[t + 2] & 0xFFFFFF;
+        issue_tile(kbase, jn, k_ring[(t + 2) % RK]);
+        issue_tile(vbase, jn, v_ring[(t + 2) % RK]);
+      }
+      const int e = list[t];
+      if (valid && ((e >> (24 + blk)) & 1)) process(k_ring[t % RK], v_ring[t % RK], e & 0xFFFFFF);
+    }
+  }
+
+  // ---- dQ = scale * acc (bf16); lane holds query column l16, d rows 4g4+r ----
+  if (valid) {
+#pragma unroll
+    for (int qs = 0; qs < NQS; ++qs) {
+      const int qq = q0 + 16 * qs + l16;
+      if (qq >= p.nq) continue;
+      __bf16* row = p.dq + (qrow0 + qq) * D;
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        bf16x4 t;
+        t[0] = to_bf16(acc[ds][qs][0] * p.scale);
+        t[1] = to_bf16(acc[ds][qs][1] * p.scale);
+        t[2] = to_bf16(acc[ds][qs][2] * p.scale);
+        t[3] = to_bf16(acc[ds][qs][3] * p.scale);
+        *(bf16x4*)(row + 16 * ds + 4 * g4) = t;
+      }
+    }
+  }
+}
+
+template <int D, bool kTest, bool kStats>
+hipError_t launch_all(const BwdParams& p, hipStream_t stream) {
+  const long long prows = (long long)p.batch * p.heads_q * p.tr * 64;
+  const long long pre_threads = prows * (D / 8);
   hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((pre_threads + 255) / 256)), dim3(256),
                      0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 grid((unsigned)((long long)p.npair * p.batch * p.heads_kv)), block(512);
-  if (test)
-    hipLaunchKernelGGL((bwd_main_kernel<D, true>), grid, block, 0, stream, p);
-  else
-    hipLaunchKernelGGL((bwd_main_kernel<D, false>), grid, block, 0, stream, p);
+  hipLaunchKernelGGL((bwd_kv_kernel<D, kTest, kStats>),
+                     dim3((unsigned)((long long)p.npair * p.batch * p.heads_kv)), dim3(256), 0,
+                     stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const long long n8 = rows * D / 8;
-  hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream,
-                     p);
+  const long long nblocks = (long long)p.n_ig * p.batch * p.heads_kv * p.n_hg;
+  hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)nblocks), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_d(const BwdParams& p, bool test, hipStream_t stream) {
+  const bool stats = p.counters != nullptr || p.decisions != nullptr;
+  if (test)
+    return stats ? launch_all<D, true, true>(p, stream) : launch_all<D, true, false>(p, stream);
+  return stats ? launch_all<D, false, true>(p, stream) : launch_all<D, false, false>(p, stream);
+}
+
 }  // namespace
+
+size_t bwd_workspace_bytes(int batch, int heads_q, int nq, int nk, int causal) {
+  const size_t tr = (size_t)(nq + 63) / 64, tc = (size_t)(nk + 63) / 64;
+  const size_t rowinfo = (size_t)batch * heads_q * tr * kRowInfo * sizeof(float);
+  const size_t per_head = causal ? tr * (tr + 1) / 2 : tr * tc;
+  const size_t dmap = (size_t)batch * heads_q * per_head;
+  return ((rowinfo + 255) & ~(size_t)255) + ((dmap + 255) & ~(size_t)255);
+}
 
 hipError_t launch_bwd(const BwdArgs& a, bool test, hipStream_t stream) {
   BwdParams p;
@@ -468,8 +727,6 @@ hipError_t launch_bwd(const BwdArgs& a, bool test, hipStream_t stream) {
   p.dq = (__bf16*)a.dq;
   p.dk = (__bf16*)a.dk;
   p.dv = (__bf16*)a.dv;
-  p.delta = a.delta;
-  p.dq_accum = a.dq_accum;
   p.batch = a.batch;
   p.heads_q = a.heads_q;
   p.heads_kv = a.heads_kv;
@@ -483,9 +740,25 @@ hipError_t launch_bwd(const BwdArgs& a, bool test, hipStream_t stream) {
   p.tr = (a.nq + 63) / 64;
   p.tc = (a.nk + 63) / 64;
   p.npair = (p.tc + 1) / 2;
+  p.dmap_per_head = p.causal ? (long long)p.tr * (p.tr + 1) / 2 : (long long)p.tr * p.tc;
+  const size_t rowinfo = (size_t)a.batch * a.heads_q * (size_t)p.tr * kRowInfo * sizeof(float);
+  p.rowinfo = (float*)a.workspace;
+  p.dmap = (uint8_t*)a.workspace + ((rowinfo + 255) & ~(size_t)255);
+  if (p.group % 4 == 0) {
+    p.hpw = 4;
+    p.ipw = 1;
+  } else if (p.group % 2 == 0) {
+    p.hpw = 2;
+    p.ipw = 2;
+  } else {
+    p.hpw = 1;
+    p.ipw = 4;
+  }
+  p.n_hg = p.group / p.hpw;
+  p.n_ig = (p.tr + p.ipw - 1) / p.ipw;
   p.counters = a.counters;
   p.decisions = a.decisions;
-  return a.head_dim == 128 ? launch_all<128>(p, test, stream) : launch_all<64>(p, test, stream);
+  return a.head_dim == 128 ? launch_d<128>(p, test, stream) : launch_d<64>(p, test, stream);
 }
 
 }  // namespace mala

@@ -108,19 +108,36 @@ __device__ __forceinline__ void vmcnt_wait() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// vmcnt wait with a run-time (wave-uniform) count: branches to the constant
-// wait for the largest supported count <= n (waiting for more is safe).
+// vmcnt wait with a run-time (wave-uniform) count: waits for the largest
+// supported count <= n (waiting for more than needed is always safe).
 __device__ __forceinline__ void vmcnt_wait_le(int n) {
-  if (n <= 0) vmcnt_wait<0>();
-  else if (n == 1) vmcnt_wait<1>();
-  else if (n == 2) vmcnt_wait<2>();
-  else if (n == 3) vmcnt_wait<3>();
-  else if (n < 8) vmcnt_wait<4>();
-  else if (n < 16) vmcnt_wait<8>();
-  else if (n < 18) vmcnt_wait<16>();
-  else if (n < 20) vmcnt_wait<18>();
-  else if (n < 21) vmcnt_wait<20>();
-  else vmcnt_wait<21>();
+  switch (n < 0 ? 0 : (n > 24 ? 24 : n)) {
+    case 0: vmcnt_wait<0>(); break;
+    case 1: vmcnt_wait<1>(); break;
+    case 2: vmcnt_wait<2>(); break;
+    case 3: vmcnt_wait<3>(); break;
+    case 4: vmcnt_wait<4>(); break;
+    case 5: vmcnt_wait<5>(); break;
+    case 6: vmcnt_wait<6>(); break;
+    case 7: vmcnt_wait<7>(); break;
+    case 8: vmcnt_wait<8>(); break;
+    case 9: vmcnt_wait<9>(); break;
+    case 10: vmcnt_wait<10>(); break;
+    case 11: vmcnt_wait<11>(); break;
+    case 12: vmcnt_wait<12>(); break;
+    case 13: vmcnt_wait<13>(); break;
+    case 14: vmcnt_wait<14>(); break;
+    case 15: vmcnt_wait<15>(); break;
+    case 16: vmcnt_wait<16>(); break;
+    case 17: vmcnt_wait<17>(); break;
+    case 18: vmcnt_wait<18>(); break;
+    case 19: vmcnt_wait<19>(); break;
+    case 20: vmcnt_wait<20>(); break;
+    case 21: vmcnt_wait<21>(); break;
+    case 22: vmcnt_wait<22>(); break;
+    case 23: vmcnt_wait<23>(); break;
+    default: vmcnt_wait<24>(); break;
+  }
 }
 
 // ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
@@ -154,5 +171,15 @@ __device__ __forceinline__ int v_swz(int d) { return (d ^ (d >> 3)) & 7; }
 // Row-major tiles read with the transposing read (4 consecutive rows x 2
 // chunks per 16-lane group): even row offsets keep the 8 chunks distinct.
 __device__ __forceinline__ int tr_swz(int row) { return (row << 1) ^ ((row >> 3) & 1); }
+// Tiles read both ways: row-major MFMA operand reads whose 16 rows are the
+// permuted set 32a + 8(R/4) + 4c + R%4 (R = 0..15), and transposing reads of
+// 4 consecutive rows x 16 columns per 16-lane group. Chunk bits 1-3 follow
+// row bits 0, 1, 3 (distinct chunks for the transposing reads) and bit 0
+// row bits 3 ^ 4 (distinct for the 8- and 16-row groups of the row-major
+// reads); with 256-byte rows (d = 128) both access kinds are free of bank
+// conflicts for 32 or 64 four-byte banks.
+__device__ __forceinline__ int dsw(int row) {
+  return (((row >> 3) ^ (row >> 4)) & 1) | ((row & 3) << 1) | (((row >> 3) & 1) << 3);
+}
 
 }  // namespace mala

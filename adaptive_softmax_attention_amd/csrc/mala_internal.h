@@ -30,8 +30,7 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;     // [B][Hq][Nq] fp32 workspace: rowsum(O o dO)
-  float* dq_accum;  // [B][Hq][Nq][D] fp32 workspace
+  void* workspace;  // bwd_workspace_bytes(): per-block row terms + decision map
   int batch, heads_q, heads_kv, nq, nk, head_dim;
   int causal;
   float scale;
@@ -63,7 +62,7 @@ hipError_t launch_fwd(const FwdArgs& a, bool test, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, bool test, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, bool test, hipStream_t stream);
 
-size_t bwd_workspace_bytes(int batch, int heads_q, int nq, int head_dim);
+size_t bwd_workspace_bytes(int batch, int heads_q, int nq, int nk, int causal);
 size_t decode_workspace_bytes(int batch, int heads_q, int num_splits, int head_dim);
 
 }  // namespace mala

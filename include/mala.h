@@ -111,18 +111,23 @@ int mala_fwd(const mala_shape* shape, const mala_config* cfg, const void* q, con
 int fullattn_fwd(const mala_shape* shape, const mala_config* cfg, const void* q, const void* k,
                  const void* v, void* o, float* lse, const mala_stats* stats, void* stream);
 
-/* Bytes of device workspace mala_bwd / fullattn_bwd need (fp32 row terms
- * D = rowsum(O o dO) and an fp32 dQ accumulator). Returns 0 for an invalid
- * shape or config. */
+/* Bytes of device workspace mala_bwd / fullattn_bwd need: fp32 row terms
+ * per 64-row query block (z = LSE in log2 units, the test threshold and
+ * D = rowsum(O o dO); 1 KiB per block) and one decision byte per legal tile
+ * (the lower triangle when causal). Returns 0 for an invalid shape or
+ * config. */
 size_t mala_bwd_workspace_bytes(const mala_shape* shape, const mala_config* cfg);
 
 /* MALA backward (Algorithm 2; Eq. 4; the backward part of Appendix A.1).
- * Key-major: per (batch, KV head, key block), query blocks are
- * visited for every query head of the group. Q.K is recomputed; a tile is
- * skipped when every legal entry has s - z_q < log(tau / L_q), with z = the
- * forward's LSE; otherwise P = exp(s - z), dP = dO V^T,
- * dS = P o (dP - rowsum(O o dO)) and the dV, dK, dQ products run. o and lse
- * are the forward's outputs. dQ, dK, dV are overwritten. workspace must hold
+ * A key-major pass visits, per (batch, KV head, pair of key blocks), every
+ * query block with a legal entry for every query head of the group; Q.K is
+ * recomputed and a tile is skipped when every legal entry has
+ * s - z_q < log(tau / L_q), with z = the forward's LSE; otherwise
+ * P = exp(s - z), dP = dO V^T, dS = P o (dP - rowsum(O o dO)) and the dV and
+ * dK products run. The decisions are stored in the workspace and a
+ * query-major pass forms dQ over the kept tiles only (deterministic: no
+ * atomics). o and lse are the forward's outputs. dQ, dK, dV are
+ * overwritten (rows without a kept tile get zeros). workspace must hold
  * mala_bwd_workspace_bytes(); its contents on entry are irrelevant. */
 int mala_bwd(const mala_shape* shape, const mala_config* cfg, const void* q, const void* k,
              const void* v, const void* o, const float* lse, const void* dout, void* dq,

@@ -104,9 +104,15 @@ def test_valid_call_without_device_reports_device_error():
 def test_workspace_sizes():
     L = m.lib()
     s, c = shape(B=2, Hq=4, Nq=100, Nk=100, d=64), cfg()
-    rows = 2 * 4 * 100
     a256 = lambda x: (x + 255) // 256 * 256
-    assert L.mala_bwd_workspace_bytes(ctypes.byref(s), ctypes.byref(c)) == a256(rows * 4) + a256(rows * 64 * 4)
+    # backward: 1 KiB of row terms per 64-row query block, plus one decision
+    # byte per legal tile (lower triangle when causal, Tr x Tc otherwise)
+    bh, tr = 2 * 4, 2
+    want = a256(bh * tr * 1024) + a256(bh * tr * (tr + 1) // 2)
+    assert L.mala_bwd_workspace_bytes(ctypes.byref(s), ctypes.byref(c)) == want
+    s2 = shape(B=1, Hq=2, Hkv=1, Nq=130, Nk=700, d=128)
+    want = a256(2 * 3 * 1024) + a256(2 * 3 * 11)
+    assert L.mala_bwd_workspace_bytes(ctypes.byref(s2), ctypes.byref(cfg(causal=0))) == want
     assert L.mala_bwd_workspace_bytes(ctypes.byref(shape(d=96)), ctypes.byref(c)) == 0
     sd = shape(B=3, Hq=8, Hkv=2, Nq=1, Nk=1000, d=128)
     n = 3 * 8 * 5

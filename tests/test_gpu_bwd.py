@@ -108,7 +108,7 @@ def compare_bwd(inp, tau, causal=True, sel_q=None, sel_k=None, fwd_sel=None, lab
         assert ok, f"{name} V1 worst ratio {worst}"
         r2 = v2(x, bbf[name][rows])
         assert r2 <= V2_TOL, f"{name} V2 {r2}"
-        ok, rl2 = l2_ok(x, bex[name][rows], bmag[name][rows])
+        ok, rl2 = l2_ok(x, bex[name][rows], bmag[name][rows], bmd[name][rows])
         assert ok, f"{name} relative L2 vs fp64 {rl2}"
         assert np.isfinite(x).all()
         out[name + "_v2"] = r2
