@@ -128,19 +128,28 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 
 // ----------------------------------------------------------------- kv ----
 template <int D, bool kTest, bool kStats>
-__global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
-  constexpr int NDC = D / 32;           // reduction chunks over d
-  constexpr int NDS = D / 16;           // 16-column subtiles of d
-  constexpr int KCH = D / 8;            // 16-byte chunks per row
-  constexpr int QCPT = 64 * KCH / 128;  // copies per lane per tile (2 waves copy)
-  constexpr int RQ = 4;                 // Q ring: current, deferred, 2 ahead
-  constexpr int PF = 2;                 // Q prefetch distance (items)
+__global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdParams p) {
+  constexpr int NT = 512;                // 8 wave64s, two per SIMD
+  constexpr int NDC = D / 32;            // reduction chunks over d
+  constexpr int NDS = D / 16;            // 16-column subtiles of d
+  constexpr int KCH = D / 8;             // 16-byte chunks per row
+  constexpr int TB = 64 * D * 2;         // bytes of a 64-row tile
+  constexpr int RB = kRowInfo * 4;       // bytes of a block's row terms
+  constexpr int CPW = TB / 16 / NT;      // 16-byte copies per lane per tile
+  constexpr int PF = 4;                  // scoring phase: Q tiles in flight (items)
+  constexpr int RQ = PF + 1;             // scoring ring: PF in flight + the one in use
+  constexpr int PFP = 2;                 // post phase: prefetch distance (kept items)
+  constexpr int RP = PFP + 1;
+  constexpr int SQ = TB + RB;            // scoring slot: Q, row terms
+  constexpr int SP = 2 * TB + RB;        // post slot: Q, dO, row terms
+  constexpr int RING = (RQ * SQ > RP * SP) ? RQ * SQ : RP * SP;
+  constexpr int CH = 2048;               // items per chunk (decisions held in LDS)
 
-  __shared__ __attribute__((aligned(16))) __bf16 q_ring[RQ][64 * D];
-  __shared__ __attribute__((aligned(16))) float ri_ring[RQ][kRowInfo];
-  __shared__ __attribute__((aligned(16))) __bf16 do_ring[2][64 * D];
-  __shared__ __attribute__((aligned(16))) __bf16 v_lds[128 * D];  // V of the 128 keys
-  __shared__ int flags[4];
+  __shared__ __attribute__((aligned(16))) char ring[RING];
+  __shared__ uint8_t dec_lds[2][CH];
+  __shared__ int list[CH];
+  __shared__ int flags[2][8];
+  __shared__ int wcount[8];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -153,44 +162,28 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   const int b = bk / p.heads_kv, kvh = bk % p.heads_kv;
   const int j0 = 2 * J;
   const bool has1 = j0 + 1 < p.tc;  // the second key block exists
-  const int kb = w >> 1;            // this wave's key block: 2J + kb
+  const int kb = w >> 2;            // this wave's key block: 2J + kb
   const int jw = j0 + kb;
   const __bf16* kbase = p.k + (size_t)bk * p.nk * D;
   const __bf16* vbase = p.v + (size_t)bk * p.nk * D;
 
-  // K of this wave's 32 keys (two 16-key subtiles) as B operands in
-  // registers; V of the workgroup's 128 keys in LDS (read by kept items
-  // only), 16-byte chunks XOR-swizzled by the key row so that 16
-  // consecutive rows of one chunk hit distinct banks
-  int key[2];
-  bf16x8 kreg[2][NDC];
+  // K and V of this wave's 16 keys as B operands
+  const int key = 64 * jw + 16 * (w & 3) + l16;
+  bf16x8 kreg[NDC], vreg[NDC];
+  {
+    const bool ok = key < p.nk;
 #pragma unroll
-  for (int ns = 0; ns < 2; ++ns) {
-    key[ns] = 64 * jw + 32 * (w & 1) + 16 * ns + l16;
-    const bool ok = key[ns] < p.nk;
-#pragma unroll
-    for (int dc = 0; dc < NDC; ++dc)
-      kreg[ns][dc] =
-          ok ? *(const bf16x8*)(kbase + (size_t)key[ns] * D + 32 * dc + 8 * g4) : bf16x8{};
-  }
-#pragma unroll
-  for (int x = 0; x < 128 * KCH / 256; ++x) {
-    const int c = x * 256 + tid;
-    const int row = c / KCH, ch = c % KCH;
-    const int kk = 64 * j0 + row;
-    const bf16x8 val = kk < p.nk ? *(const bf16x8*)(vbase + (size_t)kk * D + 8 * ch) : bf16x8{};
-    *(bf16x8*)(v_lds + row * D + ((ch ^ row) & (KCH - 1)) * 8) = val;
-  }
-  // (the first barrier of the item loop orders these stores before any read)
-
-  floatx4 dk_acc[2][NDS], dv_acc[2][NDS];
-#pragma unroll
-  for (int ns = 0; ns < 2; ++ns)
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
-      dk_acc[ns][ds] = floatx4{0.f, 0.f, 0.f, 0.f};
-      dv_acc[ns][ds] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int dc = 0; dc < NDC; ++dc) {
+      kreg[dc] = ok ? *(const bf16x8*)(kbase + (size_t)key * D + 32 * dc + 8 * g4) : bf16x8{};
+      vreg[dc] = ok ? *(const bf16x8*)(vbase + (size_t)key * D + 32 * dc + 8 * g4) : bf16x8{};
     }
+  }
+  floatx4 dk_acc[NDS], dv_acc[NDS];
+#pragma unroll
+  for (int ds = 0; ds < NDS; ++ds) {
+    dk_acc[ds] = floatx4{0.f, 0.f, 0.f, 0.f};
+    dv_acc[ds] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
 
   // items: query blocks from the last one down to the first with a legal
   // entry for key block 2J, query heads of the group innermost
@@ -198,260 +191,310 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   const int n_items = p.group * (p.tr - i_lo);
   auto item_i = [&](int it) { return p.tr - 1 - it / p.group; };
   auto item_h = [&](int it) { return kvh * p.group + it % p.group; };
+  auto legal1 = [&](int i) { return has1 && (!p.causal || i > j0); };
 
-  // ---- async copies of a 64-row tile (rows past the end re-read the last
-  //      row: their row terms make them inert) ----
-  auto issue_rows = [&](const __bf16* src, int i, __bf16* slot, int cw) {
+  // ---- asynchronous tile copies: each wave moves an eighth of a tile and
+  //      of the row terms, so every wave issues CPW + 1 copies per tile ----
+  uint32_t toff[CPW];  // byte offset within a full tile, per copy
 #pragma unroll
-    for (int x = 0; x < QCPT; ++x) {
-      const int s0 = (2 * x + cw) * 64;  // first 16-byte chunk of this copy
-      const int s = s0 + lane;
-      const int row = s / KCH, pc = s % KCH;
-      const int qq = min(64 * i + row, p.nq - 1);
-      async_copy16(src + (size_t)qq * D + ((pc ^ dsw(row)) & (KCH - 1)) * 8, slot + s0 * 8);
+  for (int x = 0; x < CPW; ++x) {
+    const int s = (8 * x + w) * 64 + lane;  // 16-byte chunk this lane fetches
+    const int row = s / KCH, pc = s % KCH;
+    toff[x] = (uint32_t)(row * D * 2 + ((pc ^ dsw(row)) & (KCH - 1)) * 16);
+  }
+  auto copy_tile = [&](const __bf16* rows0, int i, char* slot) {
+    // rows0: row 0 of (b, h); block i lands swizzled in slot
+    if (64 * i + 64 <= p.nq) {
+      const char* src = (const char*)(rows0 + (size_t)64 * i * D);
+#pragma unroll
+      for (int x = 0; x < CPW; ++x) async_copy16_so(src, toff[x], slot + (8 * x + w) * 1024);
+    } else {  // ragged last block: rows past the end re-read the last row
+#pragma unroll
+      for (int x = 0; x < CPW; ++x) {
+        const int s = (8 * x + w) * 64 + lane;
+        const int row = s / KCH, pc = s % KCH;
+        const int qq = min(64 * i + row, p.nq - 1);
+        async_copy16(rows0 + (size_t)qq * D + ((pc ^ dsw(row)) & (KCH - 1)) * 8,
+                     slot + (8 * x + w) * 1024);
+      }
     }
   };
-  auto issue_q = [&](int it) {  // waves 0 and 1
-    const int i = item_i(it), h = item_h(it), slot = it % RQ;
-    issue_rows(p.q + (size_t)(b * p.heads_q + h) * p.nq * D, i, q_ring[slot], w);
-    if (w == 0)
-      async_copy16(p.rowinfo + ((size_t)(b * p.heads_q + h) * p.tr + i) * kRowInfo + 4 * lane,
-                   ri_ring[slot]);
+  auto copy_rowinfo = [&](int h, int i, char* slot) {
+    const float* src = p.rowinfo + ((size_t)(b * p.heads_q + h) * p.tr + i) * kRowInfo;
+    if (lane < 8) async_copy16_so(src, (uint32_t)(128 * w + 16 * lane), slot + 128 * w);
   };
-  auto issue_do = [&](int it) {  // waves 2 and 3
-    const int i = item_i(it), h = item_h(it);
-    issue_rows(p.dout + (size_t)(b * p.heads_q + h) * p.nq * D, i, do_ring[it & 1], w - 2);
-  };
-  // memory operations of waves 0 / 1 per item: the Q copy (+ the row terms
-  // on wave 0) and, on wave 0, one decision store
-  const int cq = QCPT + (w == 0 ? 1 : 0);
+  auto q_rows0 = [&](int h) { return p.q + (size_t)(b * p.heads_q + h) * p.nq * D; };
+  auto do_rows0 = [&](int h) { return p.dout + (size_t)(b * p.heads_q + h) * p.nq * D; };
 
   // A operand: rows qperm(qs, l16) of a row-major tile, reduction chunk dc
-  auto a_rows = [&](const __bf16* t, int qs, int dc) {
+  auto a_rows = [&](const char* t, int qs, int dc) {
     const int row = qperm(qs, l16);
     const int ch = 4 * dc + g4;
-    return *(const bf16x8*)(t + row * D + ((ch ^ dsw(row)) & (KCH - 1)) * 8);
+    return *(const bf16x8*)(t + row * D * 2 + ((ch ^ dsw(row)) & (KCH - 1)) * 16);
   };
   // B operand: column 16 ds + l16 of a row-major tile over the 8 rows
   // 32 kc + 8 g4 + 0..7, from two transposing reads
-  auto b_cols = [&](const __bf16* t, int kc, int ds) {
+  auto b_cols = [&](const char* t, int kc, int ds) {
     short4v h2[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const int row = 32 * kc + 8 * g4 + 4 * hh + (l16 >> 2);
       const int col = 16 * ds + 4 * (l16 & 3);
-      h2[hh] = lds_read_tr4(t + row * D + (((col >> 3) ^ dsw(row)) & (KCH - 1)) * 8 + (col & 7));
+      h2[hh] = lds_read_tr4((const __bf16*)(t + row * D * 2 +
+                                            (((col >> 3) ^ dsw(row)) & (KCH - 1)) * 16 +
+                                            (col & 7) * 2));
     }
     return join_tr(h2[0], h2[1]);
   };
-
-  // post-score work of a kept item, one half of the 64 queries (query
-  // subtiles 2kc, 2kc + 1) at a time
-  auto post = [&](int itp, const floatx4(&sp)[4][2]) {
-    const __bf16* qt = q_ring[itp % RQ];
-    const __bf16* dt = do_ring[itp & 1];
-    const float* ri = ri_ring[itp % RQ];
+  // causal mask at the diagonal and the ragged key tail
+  auto mask_scores = [&](floatx4 sv, int i, int qs) {
+    floatx4 out;
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      // dP = dO V^T for query subtiles 2kc, 2kc + 1 (same layout as S)
-      floatx4 dp[2][2];
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        dp[x][0] = floatx4{0.f, 0.f, 0.f, 0.f};
-        dp[x][1] = floatx4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int dc = 0; dc < NDC; ++dc) {
-        bf16x8 bv[2];
-#pragma unroll
-        for (int ns = 0; ns < 2; ++ns) {
-          const int row = 64 * kb + 32 * (w & 1) + 16 * ns + l16;
-          const int ch = 4 * dc + g4;
-          bv[ns] = *(const bf16x8*)(v_lds + row * D + ((ch ^ row) & (KCH - 1)) * 8);
-        }
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          const bf16x8 a = a_rows(dt, 2 * kc + x, dc);
-          dp[x][0] = mfma16x16x32(a, bv[0], dp[x][0]);
-          dp[x][1] = mfma16x16x32(a, bv[1], dp[x][1]);
-        }
-      }
-      // P = exp2(s c - z2), dS = P (dP - D), packed as A operands [key][query]
-      bf16x8 pa[2], da[2];
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        const int qs = 2 * kc + x;
-        const int ql = 32 * kc + 8 * g4 + 4 * x;
-        const float4 z4 = *(const float4*)(ri + ql);
-        const float4 d4 = *(const float4*)(ri + 128 + ql);
-        const float zz[4] = {z4.x, z4.y, z4.z, z4.w};
-        const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-        for (int ns = 0; ns < 2; ++ns)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float pv = fast_exp2(sp[qs][ns][r] * p.c - zz[r]);
-            const float dsv = pv * (dp[x][ns][r] - dd[r]);
-            pa[ns][4 * x + r] = to_bf16(pv);
-            da[ns][4 * x + r] = to_bf16(dsv);
-          }
-      }
-      // dV += P^T dO, dK += dS^T Q over these 32 queries
-#pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
-        const bf16x8 bo = b_cols(dt, kc, ds);
-        const bf16x8 bq = b_cols(qt, kc, ds);
-#pragma unroll
-        for (int ns = 0; ns < 2; ++ns) {
-          dv_acc[ns][ds] = mfma16x16x32(pa[ns], bo, dv_acc[ns][ds]);
-          dk_acc[ns][ds] = mfma16x16x32(da[ns], bq, dk_acc[ns][ds]);
-        }
-      }
+    for (int r = 0; r < 4; ++r) {
+      const int qq = 64 * i + qperm(qs, 4 * g4 + r);
+      const bool ill = key >= p.nk || (p.causal && key > qq);
+      out[r] = ill ? -INFINITY : sv[r];
+    }
+    return out;
+  };
+  auto advance = [&](int& i_, int& hh_) {
+    if (++hh_ == p.group) {
+      hh_ = 0;
+      --i_;
     }
   };
 
-  // ---- software pipeline over the items ----
-  if (w < 2 && n_items > 0) {
-    issue_q(0);
-    if (n_items > 1) issue_q(1);
-  }
-  bool pend = false;  // some block kept the previous item (its dO was requested)
-  bool pret = false;  // this wave's block kept the previous item
-  floatx4 sp[4][2];   // previous item's scores
-#pragma unroll
-  for (int qs = 0; qs < 4; ++qs) {
-    sp[qs][0] = floatx4{0.f, 0.f, 0.f, 0.f};
-    sp[qs][1] = floatx4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int c0 = 0; c0 < n_items; c0 += CH) {
+    const int nc = min(n_items - c0, CH);
 
-  for (int it = 0; it < n_items; ++it) {
-    const int i = item_i(it), h = item_h(it);
-    // Q(it) complete on the copying waves. Issued after it: Q(it + 1) and,
-    // on wave 0, the decision stores of the two previous items.
-    if (kStats) {
-      vmcnt_wait<0>();
-    } else if (w < 2) {
-      vmcnt_wait_le((it + 1 < n_items ? cq : 0) + (w == 0 ? min(it, 2) : 0));
+    // ======== scoring phase: every item of the chunk ========
+    lds_barrier();  // the previous chunk's post phase is done with the ring
+    int f_i = item_i(c0), f_hh = c0 % p.group;  // next item to fetch
+    int cur_i = f_i;                              // item being scored
+    int cur_hh = f_hh;
+    for (int x = 0; x < PF && x < nc; ++x) {
+      const int h = kvh * p.group + f_hh;
+      copy_tile(q_rows0(h), f_i, ring + x * SQ);
+      copy_rowinfo(h, f_i, ring + x * SQ + TB);
+      advance(f_i, f_hh);
     }
-    lds_barrier();  // Q(it) visible; every wave is done with item it - 1
-    if (w < 2 && it + PF < n_items) issue_q(it + PF);
-
-    const __bf16* qt = q_ring[it % RQ];
-    const float* ri = ri_ring[it % RQ];
-    // block 2J has a legal entry for every item; block 2J + 1 from i > 2J on
-    const bool part1 = has1 && (!p.causal || i > j0);
-    const bool part = kb == 0 || part1;
-    floatx4 s[4][2];
+    for (int k = 0; k < nc; ++k) {
+      const int i = cur_i;
+      advance(cur_i, cur_hh);
+      // Q of item k landed: at most the PF - 1 later tiles (CPW + 1 copies each) pending
+      if (kStats || k + PF > nc)
+        vmcnt_wait<0>();
+      else
+        vmcnt_wait<(CPW + 1) * (PF - 1)>();
+      lds_barrier();  // Q of item k visible; flags of item k - 1 visible
+      if (k >= 1 && tid < 2) {
+        // (a block without a legal entry wrote 0 flags)
+        const int f = (k - 1) & 1;
+        dec_lds[tid][k - 1] =
+            (flags[f][4 * tid] | flags[f][4 * tid + 1] | flags[f][4 * tid + 2] |
+             flags[f][4 * tid + 3]) != 0 ? 1 : 0;
+      }
+      if (k + PF < nc) {
+        char* slot = ring + ((k + PF) % RQ) * SQ;
+        const int h = kvh * p.group + f_hh;
+        copy_tile(q_rows0(h), f_i, slot);
+        copy_rowinfo(h, f_i, slot + TB);
+        advance(f_i, f_hh);
+      }
+      bool want = false;
+      if (kb == 0 || legal1(i)) {
+        const char* qt = ring + (k % RQ) * SQ;
+        const float* ri = (const float*)(qt + TB);
+        // all 16 A operands are read up front, then the 16 products
+        bf16x8 av[NDC][4];
 #pragma unroll
-    for (int qs = 0; qs < 4; ++qs) {
-      s[qs][0] = floatx4{0.f, 0.f, 0.f, 0.f};
-      s[qs][1] = floatx4{0.f, 0.f, 0.f, 0.f};
-    }
-    bool want = false;
-    if (part) {
+        for (int dc = 0; dc < NDC; ++dc)
 #pragma unroll
-      for (int dc = 0; dc < NDC; ++dc)
+          for (int qs = 0; qs < 4; ++qs) av[dc][qs] = a_rows(qt, qs, dc);
+        __builtin_amdgcn_sched_barrier(0);
+        floatx4 s[4];
 #pragma unroll
-        for (int qs = 0; qs < 4; ++qs) {
-          const bf16x8 a = a_rows(qt, qs, dc);
-          s[qs][0] = mfma16x16x32(a, kreg[0][dc], s[qs][0]);
-          s[qs][1] = mfma16x16x32(a, kreg[1][dc], s[qs][1]);
+        for (int qs = 0; qs < 4; ++qs) s[qs] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dc = 0; dc < NDC; ++dc)
+#pragma unroll
+          for (int qs = 0; qs < 4; ++qs) s[qs] = mfma16x16x32(av[dc][qs], kreg[dc], s[qs]);
+        if ((p.causal && i == jw) || (64 * jw + 64 > p.nk)) {
+#pragma unroll
+          for (int qs = 0; qs < 4; ++qs) s[qs] = mask_scores(s[qs], i, qs);
         }
-      // causal mask at the diagonal and the ragged key tail
-      const bool need_mask = (p.causal && i == jw) || (64 * jw + 64 > p.nk);
-      if (need_mask) {
+        if constexpr (kTest) {
+          // Eq. 4: keep iff some legal entry has s >= W_q (masked entries
+          // are -inf; W_q = -inf only for tau = 0, where every legal tile
+          // is kept)
+          unsigned long long hit = 0;
 #pragma unroll
-        for (int ns = 0; ns < 2; ++ns)
-#pragma unroll
-          for (int qs = 0; qs < 4; ++qs)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int qq = 64 * i + qperm(qs, 4 * g4 + r);
-              if (key[ns] >= p.nk || (p.causal && key[ns] > qq)) s[qs][ns][r] = -INFINITY;
+          for (int qs = 0; qs < 4; ++qs) {
+            const float4 w4 = *(const float4*)(ri + 64 + 32 * (qs >> 1) + 8 * g4 + 4 * (qs & 1));
+            hit |= __ballot(s[qs][0] >= w4.x);
+            hit |= __ballot(s[qs][1] >= w4.y);
+            hit |= __ballot(s[qs][2] >= w4.z);
+            hit |= __ballot(s[qs][3] >= w4.w);
+          }
+          want = hit != 0;
+        } else {
+          want = true;
+        }
+      }
+      if (lane == 0) flags[k & 1][w] = want ? 1 : 0;
+    }
+    lds_barrier();  // flags of the last item visible
+    if (tid < 2) {
+      const int f = (nc - 1) & 1;
+      dec_lds[tid][nc - 1] = (flags[f][4 * tid] | flags[f][4 * tid + 1] | flags[f][4 * tid + 2] |
+                              flags[f][4 * tid + 3]) != 0 ? 1 : 0;
+    }
+    lds_barrier();  // the chunk's decisions visible
+
+    // ---- decisions to the byte map (read by the dQ pass); list of kept items ----
+    int n_list = 0;
+    for (int x0 = 0; x0 < nc; x0 += NT) {
+      const int x = x0 + tid;
+      int mask = 0;
+      if (x < nc) {
+        const int it = c0 + x;
+        const int i = item_i(it), h = item_h(it);
+        const int bh = b * p.heads_q + h;
+        const bool l1 = legal1(i);
+        mask = dec_lds[0][x] | ((l1 ? dec_lds[1][x] : 0) << 1);
+        p.dmap[dmap_index(p, bh, i, j0)] = dec_lds[0][x];
+        if (l1) p.dmap[dmap_index(p, bh, i, j0 + 1)] = dec_lds[1][x];
+        if (kStats) {
+          if (p.counters) {
+            atomicAdd(&p.counters[0], l1 ? 2ull : 1ull);
+            const unsigned long long nr = (mask & 1) + ((mask >> 1) & 1);
+            if (nr) {
+              atomicAdd(&p.counters[1], nr);
+              atomicAdd(&p.counters[2], nr * (unsigned long long)min(64, p.nq - 64 * i) * 64ull);
+              atomicAdd(&p.counters[3], 1ull);
             }
-      }
-      if constexpr (kTest) {
-        // Eq. 4: keep iff some legal entry has s >= W_q (masked entries are
-        // -inf; W_q = -inf only for tau = 0, where every legal tile is kept)
-        bool wt = false;
-#pragma unroll
-        for (int qs = 0; qs < 4; ++qs) {
-          const float4 w4 = *(const float4*)(ri + 64 + 32 * (qs >> 1) + 8 * g4 + 4 * (qs & 1));
-#pragma unroll
-          for (int ns = 0; ns < 2; ++ns) {
-            wt |= s[qs][ns][0] >= w4.x;
-            wt |= s[qs][ns][1] >= w4.y;
-            wt |= s[qs][ns][2] >= w4.z;
-            wt |= s[qs][ns][3] >= w4.w;
+          }
+          if (p.decisions) {
+            p.decisions[((size_t)bh * p.tr + i) * p.tc + j0] = dec_lds[0][x];
+            if (l1) p.decisions[((size_t)bh * p.tr + i) * p.tc + j0 + 1] = dec_lds[1][x];
           }
         }
-        want = wave_any(wt);
-      } else {
-        want = true;
       }
+      const unsigned long long bal = __ballot(mask != 0);
+      const int before = __popcll(bal & ((1ull << lane) - 1ull));
+      if (lane == 0) wcount[w] = __popcll(bal);
+      lds_barrier();
+      int off = n_list;
+      for (int y = 0; y < w; ++y) off += wcount[y];
+      if (mask != 0) list[off + before] = x | (mask << 24);
+#pragma unroll
+      for (int y = 0; y < 8; ++y) n_list += wcount[y];
+      lds_barrier();  // wcount reused; list entries visible
     }
-    if (lane == 0) flags[w] = want ? 1 : 0;
-    // dO of the previous item complete (the copying waves' only stream)
-    if (kStats) {
-      vmcnt_wait<0>();
-    } else if (w >= 2 && pend) {
-      vmcnt_wait<0>();
-    }
-    lds_barrier();  // flags visible; dO(it - 1) visible
-    const bool ret0 = (flags[0] | flags[1]) != 0;
-    const bool ret1 = part1 && (flags[2] | flags[3]) != 0;
-    const bool ret = kb == 0 ? ret0 : ret1;
-    const int bh = b * p.heads_q + h;
-    if (w == 0 && lane < 2) {
-      // lane 0 always stores (block 2J is legal for every item)
-      const bool legal = lane == 0 || part1;
-      const bool r = lane == 0 ? ret0 : ret1;
-      if (legal) p.dmap[dmap_index(p, bh, i, j0 + lane)] = r ? 1 : 0;
-      if (kStats && legal) {
-        if (p.counters) {
-          atomicAdd(&p.counters[0], 1ull);
-          if (r) {
-            atomicAdd(&p.counters[1], 1ull);
-            atomicAdd(&p.counters[2], (unsigned long long)min(64, p.nq - 64 * i) * 64ull);
+    vmcnt_wait<0>();  // the decision stores are out (the post phase counts copies only)
+
+    // ======== post-score phase: kept items only, Q and dO prefetched ========
+    auto issue_post = [&](int t) {
+      const int e = list[t];
+      const int it = c0 + (e & 0xFFFFFF);
+      const int i = item_i(it), h = item_h(it);
+      char* slot = ring + (t % RP) * SP;
+      copy_tile(q_rows0(h), i, slot);
+      copy_tile(do_rows0(h), i, slot + TB);
+      copy_rowinfo(h, i, slot + 2 * TB);
+    };
+    for (int x = 0; x < PFP && x < n_list; ++x) issue_post(x);
+    for (int t = 0; t < n_list; ++t) {
+      if (kStats || t + PFP > n_list)
+        vmcnt_wait<0>();
+      else
+        vmcnt_wait<(2 * CPW + 1) * (PFP - 1)>();
+      lds_barrier();  // entry t visible; every wave is done with entry t - 1
+      if (t + PFP < n_list) issue_post(t + PFP);
+      const int e = list[t];
+      if (((e >> (24 + kb)) & 1) == 0) continue;
+      const int i = item_i(c0 + (e & 0xFFFFFF));
+      const char* qt = ring + (t % RP) * SP;
+      const char* dt = qt + TB;
+      const float* ri = (const float*)(qt + 2 * TB);
+      const bool need_mask = (p.causal && i == jw) || (64 * jw + 64 > p.nk);
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        // S (recomputed) and dP = dO V^T for query subtiles 2kc, 2kc + 1
+        bf16x8 aq[NDC][2], ao[NDC][2];
+#pragma unroll
+        for (int dc = 0; dc < NDC; ++dc)
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            aq[dc][x] = a_rows(qt, 2 * kc + x, dc);
+            ao[dc][x] = a_rows(dt, 2 * kc + x, dc);
+          }
+        __builtin_amdgcn_sched_barrier(0);
+        floatx4 s[2], dp[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          s[x] = floatx4{0.f, 0.f, 0.f, 0.f};
+          dp[x] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int dc = 0; dc < NDC; ++dc)
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            s[x] = mfma16x16x32(aq[dc][x], kreg[dc], s[x]);
+            dp[x] = mfma16x16x32(ao[dc][x], vreg[dc], dp[x]);
+          }
+        if (need_mask) {
+#pragma unroll
+          for (int x = 0; x < 2; ++x) s[x] = mask_scores(s[x], i, 2 * kc + x);
+        }
+        // P = exp2(s c - z2), dS = P (dP - D), packed as A operands [key][query]
+        bf16x8 pa, da;
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const int ql = 32 * kc + 8 * g4 + 4 * x;
+          const float4 z4 = *(const float4*)(ri + ql);
+          const float4 d4 = *(const float4*)(ri + 128 + ql);
+          const float zz[4] = {z4.x, z4.y, z4.z, z4.w};
+          const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float pv = fast_exp2(s[x][r] * p.c - zz[r]);
+            pa[4 * x + r] = to_bf16(pv);
+            da[4 * x + r] = to_bf16(pv * (dp[x][r] - dd[r]));
           }
         }
-        if (p.decisions) p.decisions[((size_t)bh * p.tr + i) * p.tc + j0 + lane] = r ? 1 : 0;
-      }
-    }
-    const bool any = ret0 || ret1;
-    if (w >= 2 && any) issue_do(it);
-    if (kStats && any && tid == 128 && p.counters) atomicAdd(&p.counters[3], 1ull);
-
-    // the previous item's post-score work (its dO arrived during this scoring)
-    if (pret) post(it - 1, sp);
-
-    pend = any;
-    pret = ret;
+        // dV += P^T dO, dK += dS^T Q over these 32 queries
 #pragma unroll
-    for (int qs = 0; qs < 4; ++qs) {
-      sp[qs][0] = s[qs][0];
-      sp[qs][1] = s[qs][1];
+        for (int dh = 0; dh < 2; ++dh) {
+          bf16x8 bo[NDS / 2], bq[NDS / 2];
+#pragma unroll
+          for (int y = 0; y < NDS / 2; ++y) {
+            bo[y] = b_cols(dt, kc, dh * (NDS / 2) + y);
+            bq[y] = b_cols(qt, kc, dh * (NDS / 2) + y);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int y = 0; y < NDS / 2; ++y) {
+            const int ds = dh * (NDS / 2) + y;
+            dv_acc[ds] = mfma16x16x32(pa, bo[y], dv_acc[ds]);
+            dk_acc[ds] = mfma16x16x32(da, bq[y], dk_acc[ds]);
+          }
+        }
+      }
     }
   }
-  // the last item's post-score work
-  if (w >= 2 && pend) vmcnt_wait<0>();
-  lds_barrier();
-  if (pret) post(n_items - 1, sp);
 
-  // ---- dK = scale * sum, dV; output rows = keys 4 g4 + r of subtile ns ----
+  // ---- dK = scale * sum, dV; output rows = keys 4 g4 + r of this wave's 16 ----
 #pragma unroll
-  for (int ns = 0; ns < 2; ++ns) {
+  for (int r = 0; r < 4; ++r) {
+    const int kk = 64 * jw + 16 * (w & 3) + 4 * g4 + r;
+    if (jw >= p.tc || kk >= p.nk) continue;
+    __bf16* dkr = p.dk + ((size_t)bk * p.nk + kk) * D;
+    __bf16* dvr = p.dv + ((size_t)bk * p.nk + kk) * D;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int kk = 64 * jw + 32 * (w & 1) + 16 * ns + 4 * g4 + r;
-      if (jw >= p.tc || kk >= p.nk) continue;
-      __bf16* dkr = p.dk + ((size_t)bk * p.nk + kk) * D;
-      __bf16* dvr = p.dv + ((size_t)bk * p.nk + kk) * D;
-#pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
-        dkr[16 * ds + l16] = to_bf16(dk_acc[ns][ds][r] * p.scale);
-        dvr[16 * ds + l16] = to_bf16(dv_acc[ns][ds][r]);
-      }
+    for (int ds = 0; ds < NDS; ++ds) {
+      dkr[16 * ds + l16] = to_bf16(dk_acc[ds][r] * p.scale);
+      dvr[16 * ds + l16] = to_bf16(dv_acc[ds][r]);
     }
   }
 }
@@ -689,7 +732,7 @@ hipError_t launch_all(const BwdParams& p, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_kv_kernel<D, kTest, kStats>),
-                     dim3((unsigned)((long long)p.npair * p.batch * p.heads_kv)), dim3(256), 0,
+                     dim3((unsigned)((long long)p.npair * p.batch * p.heads_kv)), dim3(512), 0,
                      stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

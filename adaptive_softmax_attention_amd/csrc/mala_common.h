@@ -100,6 +100,27 @@ __device__ __forceinline__ void async_copy4(const void* gsrc, void* lds_base) {
       : "memory", "m0");
 }
 
+// Same copy with a wave-uniform 64-bit base (SGPR pair) and a 32-bit
+// per-lane byte offset: no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ void async_copy16_so(const void* sbase, uint32_t voff, void* lds_base) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_base);
+  // readfirstlane returns a signed int: go through uint32_t so that the low
+  // half is zero-extended (a sign-extended low half would corrupt the high
+  // half of the address)
+  const uint64_t a = (uint64_t)(uintptr_t)sbase;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(sb), "s"(lds)
+      : "memory", "m0");
+}
+
 template <int N>
 __device__ __forceinline__ void vmcnt_wait() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -111,7 +132,7 @@ __device__ __forceinline__ void vmcnt_wait() {
 // vmcnt wait with a run-time (wave-uniform) count: waits for the largest
 // supported count <= n (waiting for more than needed is always safe).
 __device__ __forceinline__ void vmcnt_wait_le(int n) {
-  switch (n < 0 ? 0 : (n > 24 ? 24 : n)) {
+  switch (n < 0 ? 0 : (n > 48 ? 48 : n)) {
     case 0: vmcnt_wait<0>(); break;
     case 1: vmcnt_wait<1>(); break;
     case 2: vmcnt_wait<2>(); break;
@@ -136,7 +157,31 @@ __device__ __forceinline__ void vmcnt_wait_le(int n) {
     case 21: vmcnt_wait<21>(); break;
     case 22: vmcnt_wait<22>(); break;
     case 23: vmcnt_wait<23>(); break;
-    default: vmcnt_wait<24>(); break;
+    case 24: vmcnt_wait<24>(); break;
+    case 25: vmcnt_wait<25>(); break;
+    case 26: vmcnt_wait<26>(); break;
+    case 27: vmcnt_wait<27>(); break;
+    case 28: vmcnt_wait<28>(); break;
+    case 29: vmcnt_wait<29>(); break;
+    case 30: vmcnt_wait<30>(); break;
+    case 31: vmcnt_wait<31>(); break;
+    case 32: vmcnt_wait<32>(); break;
+    case 33: vmcnt_wait<33>(); break;
+    case 34: vmcnt_wait<34>(); break;
+    case 35: vmcnt_wait<35>(); break;
+    case 36: vmcnt_wait<36>(); break;
+    case 37: vmcnt_wait<37>(); break;
+    case 38: vmcnt_wait<38>(); break;
+    case 39: vmcnt_wait<39>(); break;
+    case 40: vmcnt_wait<40>(); break;
+    case 41: vmcnt_wait<41>(); break;
+    case 42: vmcnt_wait<42>(); break;
+    case 43: vmcnt_wait<43>(); break;
+    case 44: vmcnt_wait<44>(); break;
+    case 45: vmcnt_wait<45>(); break;
+    case 46: vmcnt_wait<46>(); break;
+    case 47: vmcnt_wait<47>(); break;
+    default: vmcnt_wait<48>(); break;
   }
 }
 
