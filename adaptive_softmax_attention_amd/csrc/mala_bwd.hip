@@ -126,7 +126,225 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
   }
 }
 
+// -------------------------------------------------------------- score ----
+// Offline test of every legal tile (Eq. 4), key-major. A workgroup of 8
+// wave64s (two per SIMD) owns 4 key blocks (256 keys) of one KV head; wave w
+// holds 32 keys of block w/2 as MFMA B operands. It streams the Q tiles of
+// every (query block, query head) item from the last query block down,
+// through an LDS ring filled by asynchronous copies, scores them
+// (16x16x32 bf16 MFMA, 2 products per A-operand read) and compares each
+// legal score with the row threshold W_q. A block keeps the tile when any
+// of its two waves finds s >= W_q. Decisions go to the byte map read by the
+// dK/dV and dQ passes.
+template <int D, bool kTest, bool kStats>
+__global__ __launch_bounds__(512, 1) void bwd_score_kernel(BwdParams p) {
+  constexpr int NT = 512;
+  constexpr int NDC = D / 32;
+  constexpr int KCH = D / 8;
+  constexpr int TB = 64 * D * 2;         // bytes of a 64-row tile
+  constexpr int RB = kRowInfo * 4;       // bytes of a block's row terms
+  constexpr int CPW = TB / 16 / NT;      // 16-byte copies per lane per tile
+  constexpr int PF = 4;                  // Q tiles in flight (items)
+  constexpr int RQ = PF + 1;             // ring: PF in flight + the one in use
+  constexpr int SQ = TB + RB;
+  constexpr int NB = 4;                  // key blocks per workgroup
+  constexpr int CH = 1024;               // items per chunk (decisions held in LDS)
+
+  __shared__ __attribute__((aligned(16))) char ring[RQ * SQ];
+  __shared__ uint8_t dec_lds[NB][CH];
+  __shared__ int flags[2][8];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int l16 = lane & 15, g4 = lane >> 4;
+
+  const int per = p.batch * p.heads_kv;
+  const int G4 = (int)(blockIdx.x / per);  // key blocks 4 G4 .. 4 G4 + 3, longest first
+  const int bk = (int)(blockIdx.x % per);
+  const int b = bk / p.heads_kv, kvh = bk % p.heads_kv;
+  const int jb0 = NB * G4;
+  const int jw = jb0 + (w >> 1);  // this wave's key block
+  const __bf16* kbase = p.k + (size_t)bk * p.nk * D;
+
+  // K of this wave's 32 keys (two 16-key subtiles) as B operands
+  int key[2];
+  bf16x8 kreg[2][NDC];
+#pragma unroll
+  for (int ns = 0; ns < 2; ++ns) {
+    key[ns] = 64 * jw + 32 * (w & 1) + 16 * ns + l16;
+    const bool ok = key[ns] < p.nk;
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc)
+      kreg[ns][dc] =
+          ok ? *(const bf16x8*)(kbase + (size_t)key[ns] * D + 32 * dc + 8 * g4) : bf16x8{};
+  }
+  // key block x (0..3) of this workgroup has a legal entry for query block i
+  auto legal = [&](int x, int i) {
+    const int j = jb0 + x;
+    return j < p.tc && (!p.causal || i >= j);
+  };
+
+  const int i_lo = p.causal ? jb0 : 0;
+  const int n_items = p.group * (p.tr - i_lo);
+  auto item_i = [&](int it) { return p.tr - 1 - it / p.group; };
+  auto item_h = [&](int it) { return kvh * p.group + it % p.group; };
+  auto advance = [&](int& i_, int& hh_) {
+    if (++hh_ == p.group) {
+      hh_ = 0;
+      --i_;
+    }
+  };
+
+  uint32_t toff[CPW];
+#pragma unroll
+  for (int x = 0; x < CPW; ++x) {
+    const int s = (8 * x + w) * 64 + lane;
+    const int row = s / KCH, pc = s % KCH;
+    toff[x] = (uint32_t)(row * D * 2 + ((pc ^ dsw(row)) & (KCH - 1)) * 16);
+  }
+  auto fetch = [&](int h, int i, char* slot) {
+    const __bf16* rows0 = p.q + (size_t)(b * p.heads_q + h) * p.nq * D;
+    if (64 * i + 64 <= p.nq) {
+      const char* src = (const char*)(rows0 + (size_t)64 * i * D);
+#pragma unroll
+      for (int x = 0; x < CPW; ++x) async_copy16_so(src, toff[x], slot + (8 * x + w) * 1024);
+    } else {  // ragged last block: rows past the end re-read the last row
+#pragma unroll
+      for (int x = 0; x < CPW; ++x) {
+        const int s = (8 * x + w) * 64 + lane;
+        const int row = s / KCH, pc = s % KCH;
+        const int qq = min(64 * i + row, p.nq - 1);
+        async_copy16(rows0 + (size_t)qq * D + ((pc ^ dsw(row)) & (KCH - 1)) * 8,
+                     slot + (8 * x + w) * 1024);
+      }
+    }
+    const float* ri = p.rowinfo + ((size_t)(b * p.heads_q + h) * p.tr + i) * kRowInfo;
+    if (lane < 8) async_copy16_so(ri, (uint32_t)(128 * w + 16 * lane), slot + TB + 128 * w);
+  };
+
+  for (int c0 = 0; c0 < n_items; c0 += CH) {
+    const int nc = min(n_items - c0, CH);
+    lds_barrier();  // the previous chunk's decisions are written out
+    int f_i = item_i(c0), f_hh = c0 % p.group;
+    int cur_i = f_i, cur_hh = f_hh;
+    for (int x = 0; x < PF && x < nc; ++x) {
+      fetch(kvh * p.group + f_hh, f_i, ring + x * SQ);
+      advance(f_i, f_hh);
+    }
+    for (int k = 0; k < nc; ++k) {
+      const int i = cur_i;
+      advance(cur_i, cur_hh);
+      if (kStats || k + PF > nc)
+        vmcnt_wait<0>();
+      else
+        vmcnt_wait<(CPW + 1) * (PF - 1)>();
+      lds_barrier();  // Q of item k visible; flags of item k - 1 visible
+      if (k >= 1 && tid < NB) {
+        const int f = (k - 1) & 1;
+        dec_lds[tid][k - 1] = (flags[f][2 * tid] | flags[f][2 * tid + 1]) != 0 ? 1 : 0;
+      }
+      if (k + PF < nc) {
+        fetch(kvh * p.group + f_hh, f_i, ring + ((k + PF) % RQ) * SQ);
+        advance(f_i, f_hh);
+      }
+      bool want = false;
+      if (legal(w >> 1, i)) {
+        const char* qt = ring + (k % RQ) * SQ;
+        const float* ri = (const float*)(qt + TB);
+        floatx4 s[4][2];
+#pragma unroll
+        for (int qs = 0; qs < 4; ++qs) {
+          s[qs][0] = floatx4{0.f, 0.f, 0.f, 0.f};
+          s[qs][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int dc = 0; dc < NDC; ++dc) {
+          bf16x8 av[4];
+#pragma unroll
+          for (int qs = 0; qs < 4; ++qs) {
+            const int row = qperm(qs, l16);
+            const int ch = 4 * dc + g4;
+            av[qs] = *(const bf16x8*)(qt + row * D * 2 + ((ch ^ dsw(row)) & (KCH - 1)) * 16);
+          }
+#pragma unroll
+          for (int qs = 0; qs < 4; ++qs) {
+            s[qs][0] = mfma16x16x32(av[qs], kreg[0][dc], s[qs][0]);
+            s[qs][1] = mfma16x16x32(av[qs], kreg[1][dc], s[qs][1]);
+          }
+        }
+        if ((p.causal && i == jw) || (64 * jw + 64 > p.nk)) {
+#pragma unroll
+          for (int qs = 0; qs < 4; ++qs)
+#pragma unroll
+            for (int ns = 0; ns < 2; ++ns)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int qq = 64 * i + qperm(qs, 4 * g4 + r);
+                const bool ill = key[ns] >= p.nk || (p.causal && key[ns] > qq);
+                s[qs][ns][r] = ill ? -INFINITY : s[qs][ns][r];
+              }
+        }
+        if constexpr (kTest) {
+          // keep iff some legal entry has s >= W_q (masked entries are -inf;
+          // W_q = -inf only for tau = 0, where every legal tile is kept)
+          unsigned long long hit = 0;
+#pragma unroll
+          for (int qs = 0; qs < 4; ++qs) {
+            const float4 w4 = *(const float4*)(ri + 64 + 32 * (qs >> 1) + 8 * g4 + 4 * (qs & 1));
+#pragma unroll
+            for (int ns = 0; ns < 2; ++ns) {
+              hit |= __ballot(s[qs][ns][0] >= w4.x);
+              hit |= __ballot(s[qs][ns][1] >= w4.y);
+              hit |= __ballot(s[qs][ns][2] >= w4.z);
+              hit |= __ballot(s[qs][ns][3] >= w4.w);
+            }
+          }
+          want = hit != 0;
+        } else {
+          want = true;
+        }
+      }
+      if (lane == 0) flags[k & 1][w] = want ? 1 : 0;
+    }
+    lds_barrier();  // flags of the last item visible
+    if (tid < NB) {
+      const int f = (nc - 1) & 1;
+      dec_lds[tid][nc - 1] = (flags[f][2 * tid] | flags[f][2 * tid + 1]) != 0 ? 1 : 0;
+    }
+    lds_barrier();  // the chunk's decisions visible
+    // decisions of the legal tiles to the byte map (and the instrumentation)
+    for (int x = tid; x < nc * NB; x += NT) {
+      const int kx = x / NB, jx = x % NB;
+      const int it = c0 + kx;
+      const int i = item_i(it), h = item_h(it);
+      if (!legal(jx, i)) continue;
+      const int bh = b * p.heads_q + h;
+      const uint8_t d = dec_lds[jx][kx];
+      p.dmap[dmap_index(p, bh, i, jb0 + jx)] = d;
+      if (kStats) {
+        if (p.counters) {
+          atomicAdd(&p.counters[0], 1ull);
+          if (d) {
+            atomicAdd(&p.counters[1], 1ull);
+            atomicAdd(&p.counters[2], (unsigned long long)min(64, p.nq - 64 * i) * 64ull);
+          }
+        }
+        if (p.decisions) p.decisions[((size_t)bh * p.tr + i) * p.tc + jb0 + jx] = d;
+      }
+    }
+    vmcnt_wait<0>();  // the stores are out before the next chunk's copies are counted
+  }
+}
+
 // ----------------------------------------------------------------- kv ----
+// dK, dV over the kept tiles. A workgroup of 8 wave64s owns key blocks 2J
+// and 2J + 1 (16 keys per wave, K and V as B operands, dK and dV
+// accumulated in registers). Per chunk of (query block, query head) items it
+// reads the two blocks' decisions, lists the items either block keeps, and
+// runs their post-score work with Q, dO and the row terms copied
+// asynchronously into an LDS ring a few entries ahead: S is recomputed,
+// P = exp2(s c - z2), dP = dO V^T, dS = P (dP - D), dV += P^T dO,
+// dK += dS^T Q (the transposed operands from the transposing LDS read).
 template <int D, bool kTest, bool kStats>
 __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdParams p) {
   constexpr int NT = 512;                // 8 wave64s, two per SIMD
@@ -136,19 +354,13 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdParams p) {
   constexpr int TB = 64 * D * 2;         // bytes of a 64-row tile
   constexpr int RB = kRowInfo * 4;       // bytes of a block's row terms
   constexpr int CPW = TB / 16 / NT;      // 16-byte copies per lane per tile
-  constexpr int PF = 4;                  // scoring phase: Q tiles in flight (items)
-  constexpr int RQ = PF + 1;             // scoring ring: PF in flight + the one in use
-  constexpr int PFP = 2;                 // post phase: prefetch distance (kept items)
+  constexpr int PFP = 3;                 // prefetch distance (kept items)
   constexpr int RP = PFP + 1;
-  constexpr int SQ = TB + RB;            // scoring slot: Q, row terms
-  constexpr int SP = 2 * TB + RB;        // post slot: Q, dO, row terms
-  constexpr int RING = (RQ * SQ > RP * SP) ? RQ * SQ : RP * SP;
-  constexpr int CH = 2048;               // items per chunk (decisions held in LDS)
+  constexpr int SP = 2 * TB + RB;        // ring slot: Q, dO, row terms
+  constexpr int CH = 2048;               // items per chunk
 
-  __shared__ __attribute__((aligned(16))) char ring[RING];
-  __shared__ uint8_t dec_lds[2][CH];
+  __shared__ __attribute__((aligned(16))) char ring[RP * SP];
   __shared__ int list[CH];
-  __shared__ int flags[2][8];
   __shared__ int wcount[8];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -267,91 +479,9 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdParams p) {
   for (int c0 = 0; c0 < n_items; c0 += CH) {
     const int nc = min(n_items - c0, CH);
 
-    // ======== scoring phase: every item of the chunk ========
-    lds_barrier();  // the previous chunk's post phase is done with the ring
-    int f_i = item_i(c0), f_hh = c0 % p.group;  // next item to fetch
-    int cur_i = f_i;                              // item being scored
-    int cur_hh = f_hh;
-    for (int x = 0; x < PF && x < nc; ++x) {
-      const int h = kvh * p.group + f_hh;
-      copy_tile(q_rows0(h), f_i, ring + x * SQ);
-      copy_rowinfo(h, f_i, ring + x * SQ + TB);
-      advance(f_i, f_hh);
-    }
-    for (int k = 0; k < nc; ++k) {
-      const int i = cur_i;
-      advance(cur_i, cur_hh);
-      // Q of item k landed: at most the PF - 1 later tiles (CPW + 1 copies each) pending
-      if (kStats || k + PF > nc)
-        vmcnt_wait<0>();
-      else
-        vmcnt_wait<(CPW + 1) * (PF - 1)>();
-      lds_barrier();  // Q of item k visible; flags of item k - 1 visible
-      if (k >= 1 && tid < 2) {
-        // (a block without a legal entry wrote 0 flags)
-        const int f = (k - 1) & 1;
-        dec_lds[tid][k - 1] =
-            (flags[f][4 * tid] | flags[f][4 * tid + 1] | flags[f][4 * tid + 2] |
-             flags[f][4 * tid + 3]) != 0 ? 1 : 0;
-      }
-      if (k + PF < nc) {
-        char* slot = ring + ((k + PF) % RQ) * SQ;
-        const int h = kvh * p.group + f_hh;
-        copy_tile(q_rows0(h), f_i, slot);
-        copy_rowinfo(h, f_i, slot + TB);
-        advance(f_i, f_hh);
-      }
-      bool want = false;
-      if (kb == 0 || legal1(i)) {
-        const char* qt = ring + (k % RQ) * SQ;
-        const float* ri = (const float*)(qt + TB);
-        // all 16 A operands are read up front, then the 16 products
-        bf16x8 av[NDC][4];
-#pragma unroll
-        for (int dc = 0; dc < NDC; ++dc)
-#pragma unroll
-          for (int qs = 0; qs < 4; ++qs) av[dc][qs] = a_rows(qt, qs, dc);
-        __builtin_amdgcn_sched_barrier(0);
-        floatx4 s[4];
-#pragma unroll
-        for (int qs = 0; qs < 4; ++qs) s[qs] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int dc = 0; dc < NDC; ++dc)
-#pragma unroll
-          for (int qs = 0; qs < 4; ++qs) s[qs] = mfma16x16x32(av[dc][qs], kreg[dc], s[qs]);
-        if ((p.causal && i == jw) || (64 * jw + 64 > p.nk)) {
-#pragma unroll
-          for (int qs = 0; qs < 4; ++qs) s[qs] = mask_scores(s[qs], i, qs);
-        }
-        if constexpr (kTest) {
-          // Eq. 4: keep iff some legal entry has s >= W_q (masked entries
-          // are -inf; W_q = -inf only for tau = 0, where every legal tile
-          // is kept)
-          unsigned long long hit = 0;
-#pragma unroll
-          for (int qs = 0; qs < 4; ++qs) {
-            const float4 w4 = *(const float4*)(ri + 64 + 32 * (qs >> 1) + 8 * g4 + 4 * (qs & 1));
-            hit |= __ballot(s[qs][0] >= w4.x);
-            hit |= __ballot(s[qs][1] >= w4.y);
-            hit |= __ballot(s[qs][2] >= w4.z);
-            hit |= __ballot(s[qs][3] >= w4.w);
-          }
-          want = hit != 0;
-        } else {
-          want = true;
-        }
-      }
-      if (lane == 0) flags[k & 1][w] = want ? 1 : 0;
-    }
-    lds_barrier();  // flags of the last item visible
-    if (tid < 2) {
-      const int f = (nc - 1) & 1;
-      dec_lds[tid][nc - 1] = (flags[f][4 * tid] | flags[f][4 * tid + 1] | flags[f][4 * tid + 2] |
-                              flags[f][4 * tid + 3]) != 0 ? 1 : 0;
-    }
-    lds_barrier();  // the chunk's decisions visible
-
-    // ---- decisions to the byte map (read by the dQ pass); list of kept items ----
+    // ---- list of the chunk's items that either key block keeps, from the
+    //      decision map written by the scoring pass ----
+    lds_barrier();  // the previous chunk's list and ring are no longer read
     int n_list = 0;
     for (int x0 = 0; x0 < nc; x0 += NT) {
       const int x = x0 + tid;
@@ -360,25 +490,9 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdParams p) {
         const int it = c0 + x;
         const int i = item_i(it), h = item_h(it);
         const int bh = b * p.heads_q + h;
-        const bool l1 = legal1(i);
-        mask = dec_lds[0][x] | ((l1 ? dec_lds[1][x] : 0) << 1);
-        p.dmap[dmap_index(p, bh, i, j0)] = dec_lds[0][x];
-        if (l1) p.dmap[dmap_index(p, bh, i, j0 + 1)] = dec_lds[1][x];
-        if (kStats) {
-          if (p.counters) {
-            atomicAdd(&p.counters[0], l1 ? 2ull : 1ull);
-            const unsigned long long nr = (mask & 1) + ((mask >> 1) & 1);
-            if (nr) {
-              atomicAdd(&p.counters[1], nr);
-              atomicAdd(&p.counters[2], nr * (unsigned long long)min(64, p.nq - 64 * i) * 64ull);
-              atomicAdd(&p.counters[3], 1ull);
-            }
-          }
-          if (p.decisions) {
-            p.decisions[((size_t)bh * p.tr + i) * p.tc + j0] = dec_lds[0][x];
-            if (l1) p.decisions[((size_t)bh * p.tr + i) * p.tc + j0 + 1] = dec_lds[1][x];
-          }
-        }
+        mask = p.dmap[dmap_index(p, bh, i, j0)] != 0 ? 1 : 0;
+        if (legal1(i) && p.dmap[dmap_index(p, bh, i, j0 + 1)] != 0) mask |= 2;
+        if (kStats && mask != 0 && p.counters) atomicAdd(&p.counters[3], 1ull);
       }
       const unsigned long long bal = __ballot(mask != 0);
       const int before = __popcll(bal & ((1ull << lane) - 1ull));
@@ -731,9 +845,13 @@ hipError_t launch_all(const BwdParams& p, hipStream_t stream) {
                      0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_kv_kernel<D, kTest, kStats>),
-                     dim3((unsigned)((long long)p.npair * p.batch * p.heads_kv)), dim3(512), 0,
-                     stream, p);
+  const long long per = (long long)p.batch * p.heads_kv;
+  hipLaunchKernelGGL((bwd_score_kernel<D, kTest, kStats>),
+                     dim3((unsigned)(((p.tc + 3) / 4) * per)), dim3(512), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_kv_kernel<D, kTest, kStats>), dim3((unsigned)(p.npair * per)),
+                     dim3(512), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long nblocks = (long long)p.n_ig * p.batch * p.heads_kv * p.n_hg;
