@@ -337,50 +337,46 @@ __global__ __launch_bounds__(512, 1) void bwd_score_kernel(BwdParams p) {
 }
 
 // ----------------------------------------------------------------- kv ----
-// dK, dV over the kept tiles. A workgroup of 8 wave64s owns key blocks 2J
-// and 2J + 1 (16 keys per wave, K and V as B operands, dK and dV
-// accumulated in registers). Per chunk of (query block, query head) items it
-// reads the two blocks' decisions, lists the items either block keeps, and
-// runs their post-score work with Q, dO and the row terms copied
-// asynchronously into an LDS ring a few entries ahead: S is recomputed,
-// P = exp2(s c - z2), dP = dO V^T, dS = P (dP - D), dV += P^T dO,
-// dK += dS^T Q (the transposed operands from the transposing LDS read).
+// dK, dV over the kept tiles. A workgroup of 4 wave64s owns one key block
+// (16 keys per wave; K and V as B operands, dK and dV accumulated in
+// registers); two workgroups share a CU. Per chunk of (query block, query
+// head) items it reads the block's decisions from the decision map, lists
+// the kept items, and runs their post-score work with Q, dO and the row
+// terms copied asynchronously into an LDS ring one entry ahead: S is
+// recomputed, P = exp2(s c - z2), dP = dO V^T, dS = P (dP - D),
+// dV += P^T dO, dK += dS^T Q (the transposed operands come from the
+// transposing LDS read).
 template <int D, bool kTest, bool kStats>
-__global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdParams p) {
-  constexpr int NT = 512;                // 8 wave64s, two per SIMD
+__global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdParams p) {
+  constexpr int NT = 256;                // 4 wave64s
   constexpr int NDC = D / 32;            // reduction chunks over d
   constexpr int NDS = D / 16;            // 16-column subtiles of d
   constexpr int KCH = D / 8;             // 16-byte chunks per row
   constexpr int TB = 64 * D * 2;         // bytes of a 64-row tile
   constexpr int RB = kRowInfo * 4;       // bytes of a block's row terms
   constexpr int CPW = TB / 16 / NT;      // 16-byte copies per lane per tile
-  constexpr int PFP = 3;                 // prefetch distance (kept items)
-  constexpr int RP = PFP + 1;
+  constexpr int RP = 2;                  // ring: the entry in use + the next
   constexpr int SP = 2 * TB + RB;        // ring slot: Q, dO, row terms
   constexpr int CH = 2048;               // items per chunk
 
   __shared__ __attribute__((aligned(16))) char ring[RP * SP];
   __shared__ int list[CH];
-  __shared__ int wcount[8];
+  __shared__ int wcount[4];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l16 = lane & 15, g4 = lane >> 4;
 
-  // ---- work item: key blocks (2J, 2J + 1) of (b, kvh), longest first ----
+  // ---- work item: key block j of (b, kvh), longest first ----
   const int per = p.batch * p.heads_kv;
-  const int J = (int)(blockIdx.x / per);
+  const int j = (int)(blockIdx.x / per);
   const int bk = (int)(blockIdx.x % per);
   const int b = bk / p.heads_kv, kvh = bk % p.heads_kv;
-  const int j0 = 2 * J;
-  const bool has1 = j0 + 1 < p.tc;  // the second key block exists
-  const int kb = w >> 2;            // this wave's key block: 2J + kb
-  const int jw = j0 + kb;
   const __bf16* kbase = p.k + (size_t)bk * p.nk * D;
   const __bf16* vbase = p.v + (size_t)bk * p.nk * D;
 
   // K and V of this wave's 16 keys as B operands
-  const int key = 64 * jw + 16 * (w & 3) + l16;
+  const int key = 64 * j + 16 * w + l16;
   bf16x8 kreg[NDC], vreg[NDC];
   {
     const bool ok = key < p.nk;
@@ -398,19 +394,18 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdParams p) {
   }
 
   // items: query blocks from the last one down to the first with a legal
-  // entry for key block 2J, query heads of the group innermost
-  const int i_lo = p.causal ? j0 : 0;
+  // entry for key block j, query heads of the group innermost
+  const int i_lo = p.causal ? j : 0;
   const int n_items = p.group * (p.tr - i_lo);
   auto item_i = [&](int it) { return p.tr - 1 - it / p.group; };
   auto item_h = [&](int it) { return kvh * p.group + it % p.group; };
-  auto legal1 = [&](int i) { return has1 && (!p.causal || i > j0); };
 
-  // ---- asynchronous tile copies: each wave moves an eighth of a tile and
+  // ---- asynchronous tile copies: each wave moves a quarter of a tile and
   //      of the row terms, so every wave issues CPW + 1 copies per tile ----
   uint32_t toff[CPW];  // byte offset within a full tile, per copy
 #pragma unroll
   for (int x = 0; x < CPW; ++x) {
-    const int s = (8 * x + w) * 64 + lane;  // 16-byte chunk this lane fetches
+    const int s = (4 * x + w) * 64 + lane;  // 16-byte chunk this lane fetches
     const int row = s / KCH, pc = s % KCH;
     toff[x] = (uint32_t)(row * D * 2 + ((pc ^ dsw(row)) & (KCH - 1)) * 16);
   }
@@ -419,24 +414,22 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdParams p) {
     if (64 * i + 64 <= p.nq) {
       const char* src = (const char*)(rows0 + (size_t)64 * i * D);
 #pragma unroll
-      for (int x = 0; x < CPW; ++x) async_copy16_so(src, toff[x], slot + (8 * x + w) * 1024);
+      for (int x = 0; x < CPW; ++x) async_copy16_so(src, toff[x], slot + (4 * x + w) * 1024);
     } else {  // ragged last block: rows past the end re-read the last row
 #pragma unroll
       for (int x = 0; x < CPW; ++x) {
-        const int s = (8 * x + w) * 64 + lane;
+        const int s = (4 * x + w) * 64 + lane;
         const int row = s / KCH, pc = s % KCH;
         const int qq = min(64 * i + row, p.nq - 1);
         async_copy16(rows0 + (size_t)qq * D + ((pc ^ dsw(row)) & (KCH - 1)) * 8,
-                     slot + (8 * x + w) * 1024);
+                     slot + (4 * x + w) * 1024);
       }
     }
   };
   auto copy_rowinfo = [&](int h, int i, char* slot) {
     const float* src = p.rowinfo + ((size_t)(b * p.heads_q + h) * p.tr + i) * kRowInfo;
-    if (lane < 8) async_copy16_so(src, (uint32_t)(128 * w + 16 * lane), slot + 128 * w);
+    if (lane < 16) async_copy16_so(src, (uint32_t)(256 * w + 16 * lane), slot + 256 * w);
   };
-  auto q_rows0 = [&](int h) { return p.q + (size_t)(b * p.heads_q + h) * p.nq * D; };
-  auto do_rows0 = [&](int h) { return p.dout + (size_t)(b * p.heads_q + h) * p.nq * D; };
 
   // A operand: rows qperm(qs, l16) of a row-major tile, reduction chunk dc
   auto a_rows = [&](const char* t, int qs, int dc) {
@@ -458,80 +451,55 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdParams p) {
     }
     return join_tr(h2[0], h2[1]);
   };
-  // causal mask at the diagonal and the ragged key tail
-  auto mask_scores = [&](floatx4 sv, int i, int qs) {
-    floatx4 out;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int qq = 64 * i + qperm(qs, 4 * g4 + r);
-      const bool ill = key >= p.nk || (p.causal && key > qq);
-      out[r] = ill ? -INFINITY : sv[r];
-    }
-    return out;
-  };
-  auto advance = [&](int& i_, int& hh_) {
-    if (++hh_ == p.group) {
-      hh_ = 0;
-      --i_;
-    }
-  };
 
   for (int c0 = 0; c0 < n_items; c0 += CH) {
     const int nc = min(n_items - c0, CH);
 
-    // ---- list of the chunk's items that either key block keeps, from the
-    //      decision map written by the scoring pass ----
+    // ---- list of the chunk's items this key block keeps (decision map
+    //      written by the scoring pass) ----
     lds_barrier();  // the previous chunk's list and ring are no longer read
     int n_list = 0;
     for (int x0 = 0; x0 < nc; x0 += NT) {
       const int x = x0 + tid;
-      int mask = 0;
+      bool kept = false;
       if (x < nc) {
         const int it = c0 + x;
         const int i = item_i(it), h = item_h(it);
-        const int bh = b * p.heads_q + h;
-        mask = p.dmap[dmap_index(p, bh, i, j0)] != 0 ? 1 : 0;
-        if (legal1(i) && p.dmap[dmap_index(p, bh, i, j0 + 1)] != 0) mask |= 2;
-        if (kStats && mask != 0 && p.counters) atomicAdd(&p.counters[3], 1ull);
+        kept = p.dmap[dmap_index(p, b * p.heads_q + h, i, j)] != 0;
+        if (kStats && kept && p.counters) atomicAdd(&p.counters[3], 1ull);
       }
-      const unsigned long long bal = __ballot(mask != 0);
+      const unsigned long long bal = __ballot(kept);
       const int before = __popcll(bal & ((1ull << lane) - 1ull));
       if (lane == 0) wcount[w] = __popcll(bal);
       lds_barrier();
       int off = n_list;
       for (int y = 0; y < w; ++y) off += wcount[y];
-      if (mask != 0) list[off + before] = x | (mask << 24);
-#pragma unroll
-      for (int y = 0; y < 8; ++y) n_list += wcount[y];
+      if (kept) list[off + before] = x;
+      n_list += wcount[0] + wcount[1] + wcount[2] + wcount[3];
       lds_barrier();  // wcount reused; list entries visible
     }
-    vmcnt_wait<0>();  // the decision stores are out (the post phase counts copies only)
+    vmcnt_wait<0>();  // the map reads are done (the post phase counts copies only)
 
-    // ======== post-score phase: kept items only, Q and dO prefetched ========
+    // ======== post-score work of the kept items, one entry ahead ========
     auto issue_post = [&](int t) {
-      const int e = list[t];
-      const int it = c0 + (e & 0xFFFFFF);
+      const int it = c0 + list[t];
       const int i = item_i(it), h = item_h(it);
       char* slot = ring + (t % RP) * SP;
-      copy_tile(q_rows0(h), i, slot);
-      copy_tile(do_rows0(h), i, slot + TB);
+      const size_t rows = (size_t)(b * p.heads_q + h) * p.nq * D;
+      copy_tile(p.q + rows, i, slot);
+      copy_tile(p.dout + rows, i, slot + TB);
       copy_rowinfo(h, i, slot + 2 * TB);
     };
-    for (int x = 0; x < PFP && x < n_list; ++x) issue_post(x);
+    if (n_list > 0) issue_post(0);
     for (int t = 0; t < n_list; ++t) {
-      if (kStats || t + PFP > n_list)
-        vmcnt_wait<0>();
-      else
-        vmcnt_wait<(2 * CPW + 1) * (PFP - 1)>();
-      lds_barrier();  // entry t visible; every wave is done with entry t - 1
-      if (t + PFP < n_list) issue_post(t + PFP);
-      const int e = list[t];
-      if (((e >> (24 + kb)) & 1) == 0) continue;
-      const int i = item_i(c0 + (e & 0xFFFFFF));
+      vmcnt_wait<0>();  // entry t landed (nothing later was issued yet)
+      lds_barrier();    // entry t visible; every wave is done with entry t - 1
+      if (t + 1 < n_list) issue_post(t + 1);
+      const int i = item_i(c0 + list[t]);
       const char* qt = ring + (t % RP) * SP;
       const char* dt = qt + TB;
       const float* ri = (const float*)(qt + 2 * TB);
-      const bool need_mask = (p.causal && i == jw) || (64 * jw + 64 > p.nk);
+      const bool need_mask = (p.causal && i == j) || (64 * j + 64 > p.nk);
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
         // S (recomputed) and dP = dO V^T for query subtiles 2kc, 2kc + 1
@@ -559,7 +527,13 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdParams p) {
           }
         if (need_mask) {
 #pragma unroll
-          for (int x = 0; x < 2; ++x) s[x] = mask_scores(s[x], i, 2 * kc + x);
+          for (int x = 0; x < 2; ++x)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int qq = 64 * i + qperm(2 * kc + x, 4 * g4 + r);
+              const bool ill = key >= p.nk || (p.causal && key > qq);
+              s[x][r] = ill ? -INFINITY : s[x][r];
+            }
         }
         // P = exp2(s c - z2), dS = P (dP - D), packed as A operands [key][query]
         bf16x8 pa, da;
@@ -601,8 +575,8 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(BwdParams p) {
   // ---- dK = scale * sum, dV; output rows = keys 4 g4 + r of this wave's 16 ----
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int kk = 64 * jw + 16 * (w & 3) + 4 * g4 + r;
-    if (jw >= p.tc || kk >= p.nk) continue;
+    const int kk = 64 * j + 16 * w + 4 * g4 + r;
+    if (kk >= p.nk) continue;
     __bf16* dkr = p.dk + ((size_t)bk * p.nk + kk) * D;
     __bf16* dvr = p.dv + ((size_t)bk * p.nk + kk) * D;
 #pragma unroll
@@ -850,8 +824,8 @@ hipError_t launch_all(const BwdParams& p, hipStream_t stream) {
                      dim3((unsigned)(((p.tc + 3) / 4) * per)), dim3(512), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_kv_kernel<D, kTest, kStats>), dim3((unsigned)(p.npair * per)),
-                     dim3(512), 0, stream, p);
+  hipLaunchKernelGGL((bwd_kv_kernel<D, kTest, kStats>), dim3((unsigned)(p.tc * per)),
+                     dim3(256), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long nblocks = (long long)p.n_ig * p.batch * p.heads_kv * p.n_hg;

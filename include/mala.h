@@ -84,7 +84,8 @@ typedef struct {
  *             [2] retained post-score key slots (valid rows x block_k per
  *                 retained tile: the count of Sec. 2.3 / Eq. 11),
  *             [3] V tiles loaded from HBM (forward and decode); dO tiles
- *                 loaded (backward, per 128-key workgroup tile).
+ *                 loaded by the dK/dV pass (backward: one per retained
+ *                 tile).
  *   decisions device uint8, one byte per tile, written 1 (retained) or
  *             0 (skipped) for every legal tile the call tests; other bytes
  *             are left untouched. Layout [batch][heads_q][Tr][Tc] for
