@@ -114,7 +114,8 @@ int bwd_common(const mala_shape* shape, const mala_config* cfg, const void* q, c
   if (!workspace || workspace_bytes < need) return MALA_ERR_WORKSPACE;
   const int64_t tc = (shape->seqlen_k + 63) / 64;
   const int64_t tr = (shape->seqlen_q + 63) / 64;
-  if ((int64_t)shape->batch * shape->heads_kv * tc > kMaxGrid) return MALA_ERR_UNSUPPORTED;
+  // the dK/dV pass launches up to 8 segment workgroups per key block
+  if ((int64_t)shape->batch * shape->heads_kv * tc * 8 > kMaxGrid) return MALA_ERR_UNSUPPORTED;
   if ((int64_t)shape->batch * shape->heads_q * ((tr + 3) / 4 + 1) > kMaxGrid)
     return MALA_ERR_UNSUPPORTED;
   // row-term pass: one 256-thread group per 16 (d = 64) or 8 (d = 128) padded rows
@@ -206,8 +207,9 @@ int fullattn_fwd(const mala_shape* shape, const mala_config* cfg, const void* q,
 
 size_t mala_bwd_workspace_bytes(const mala_shape* shape, const mala_config* cfg) {
   if (check_shape(shape) || check_config(cfg, false)) return 0;
-  return mala::bwd_workspace_bytes(shape->batch, shape->heads_q, shape->seqlen_q,
-                                   shape->seqlen_k, cfg->causal);
+  return mala::bwd_workspace_bytes(shape->batch, shape->heads_q, shape->heads_kv,
+                                   shape->seqlen_q, shape->seqlen_k, shape->head_dim,
+                                   cfg->causal);
 }
 
 int mala_bwd(const mala_shape* shape, const mala_config* cfg, const void* q, const void* k,

@@ -46,6 +46,13 @@ namespace mala {
 namespace {
 
 constexpr int kRowInfo = 256;  // floats of row terms per 64-row block
+// The dK/dV pass splits a key block's (query block, query head) items into at
+// most kSegMax segments of about kSegItems items, one workgroup each, so that
+// a key block that every row keeps (an attention sink) does not serialise the
+// pass; the segments' fp32 partial sums are added in a fixed order by the
+// finalize kernel (deterministic, no atomics).
+constexpr int kSegItems = 2048;
+constexpr int kSegMax = 8;
 
 struct BwdParams {
   const __bf16* q;
@@ -59,6 +66,7 @@ struct BwdParams {
   __bf16* dv;
   float* rowinfo;  // [B*Hq*Tr][kRowInfo]
   uint8_t* dmap;   // backward decisions, see dmap_index()
+  float* part;     // [B*Hkv*Tc][kSegMax][2][64][D] fp32 partial dK, dV
   int batch, heads_q, heads_kv, nq, nk, group;
   int causal;
   float scale;
@@ -76,6 +84,12 @@ struct BwdParams {
 __device__ __forceinline__ long long dmap_index(const BwdParams& p, int bh, int i, int j) {
   const long long t = p.causal ? (long long)i * (i + 1) / 2 + j : (long long)i * p.tc + j;
   return (long long)bh * p.dmap_per_head + t;
+}
+
+// Segments of key block j's items (see kSegItems).
+__device__ __forceinline__ int kv_segments(const BwdParams& p, int j) {
+  const int n = p.group * (p.tr - (p.causal ? j : 0));
+  return min(kSegMax, (n + kSegItems - 1) / kSegItems);
 }
 
 // MFMA row R of subtile x holds row 32(x/2) + 8(R/4) + 4(x%2) + R%4 of the
@@ -367,11 +381,14 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdParams p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l16 = lane & 15, g4 = lane >> 4;
 
-  // ---- work item: key block j of (b, kvh), longest first ----
+  // ---- work item: segment seg of key block j of (b, kvh), longest first ----
   const int per = p.batch * p.heads_kv;
-  const int j = (int)(blockIdx.x / per);
-  const int bk = (int)(blockIdx.x % per);
+  const int seg = (int)(blockIdx.x % kSegMax);
+  const int j = (int)(blockIdx.x / kSegMax / per);
+  const int bk = (int)(blockIdx.x / kSegMax % per);
   const int b = bk / p.heads_kv, kvh = bk % p.heads_kv;
+  const int nseg = kv_segments(p, j);
+  if (seg >= nseg) return;  // (whole workgroup, before any barrier)
   const __bf16* kbase = p.k + (size_t)bk * p.nk * D;
   const __bf16* vbase = p.v + (size_t)bk * p.nk * D;
 
@@ -396,9 +413,12 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdParams p) {
   // items: query blocks from the last one down to the first with a legal
   // entry for key block j, query heads of the group innermost
   const int i_lo = p.causal ? j : 0;
-  const int n_items = p.group * (p.tr - i_lo);
-  auto item_i = [&](int it) { return p.tr - 1 - it / p.group; };
-  auto item_h = [&](int it) { return kvh * p.group + it % p.group; };
+  const int n_all = p.group * (p.tr - i_lo);
+  const int seg_len = (n_all + nseg - 1) / nseg;
+  const int it0 = seg * seg_len;                       // this segment's items:
+  const int n_items = min(n_all, it0 + seg_len) - it0;  // it0 .. it0 + n_items - 1
+  auto item_i = [&](int it) { return p.tr - 1 - (it0 + it) / p.group; };
+  auto item_h = [&](int it) { return kvh * p.group + (it0 + it) % p.group; };
 
   // ---- asynchronous tile copies: each wave moves a quarter of a tile and
   //      of the row terms, so every wave issues CPW + 1 copies per tile ----
@@ -572,19 +592,73 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdParams p) {
     }
   }
 
-  // ---- dK = scale * sum, dV; output rows = keys 4 g4 + r of this wave's 16 ----
+  // ---- output rows = keys 4 g4 + r of this wave's 16: dK = scale * sum and
+  //      dV directly when the block has one segment, else fp32 partials ----
+  if (nseg == 1) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int kk = 64 * j + 16 * w + 4 * g4 + r;
-    if (kk >= p.nk) continue;
-    __bf16* dkr = p.dk + ((size_t)bk * p.nk + kk) * D;
-    __bf16* dvr = p.dv + ((size_t)bk * p.nk + kk) * D;
+    for (int r = 0; r < 4; ++r) {
+      const int kk = 64 * j + 16 * w + 4 * g4 + r;
+      if (kk >= p.nk) continue;
+      __bf16* dkr = p.dk + ((size_t)bk * p.nk + kk) * D;
+      __bf16* dvr = p.dv + ((size_t)bk * p.nk + kk) * D;
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
-      dkr[16 * ds + l16] = to_bf16(dk_acc[ds][r] * p.scale);
-      dvr[16 * ds + l16] = to_bf16(dv_acc[ds][r]);
+      for (int ds = 0; ds < NDS; ++ds) {
+        dkr[16 * ds + l16] = to_bf16(dk_acc[ds][r] * p.scale);
+        dvr[16 * ds + l16] = to_bf16(dv_acc[ds][r]);
+      }
+    }
+  } else {
+    float* pk = p.part + (((size_t)bk * p.tc + j) * kSegMax + seg) * 2 * 64 * D;
+    float* pv = pk + 64 * D;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * w + 4 * g4 + r;
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        pk[row * D + 16 * ds + l16] = dk_acc[ds][r];
+        pv[row * D + 16 * ds + l16] = dv_acc[ds][r];
+      }
     }
   }
+}
+
+// ----------------------------------------------------------- finalize ----
+// dK = scale * sum of the segments' partial sums, dV = their sum (segments
+// added in index order), for the key blocks split into several segments.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_kv_finalize_kernel(BwdParams p) {
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;  // 8 values each
+  const long long n = (long long)p.batch * p.heads_kv * p.tc * 64 * D / 8;
+  if (t >= n) return;
+  const long long e = t * 8;
+  const int col = (int)(e % D);
+  const int row = (int)((e / D) % 64);
+  const long long bj = e / D / 64;  // bk * Tc + j
+  const int j = (int)(bj % p.tc);
+  const long long bk = bj / p.tc;
+  const int nseg = kv_segments(p, j);
+  const int kk = 64 * j + row;
+  if (nseg == 1 || kk >= p.nk) return;
+  float ak[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float av[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int sg = 0; sg < nseg; ++sg) {
+    const float* pk = p.part + ((bj * kSegMax + sg) * 2 * 64 + row) * D + col;
+    const float* pv = pk + 64 * D;
+    const float4 k0 = *(const float4*)pk, k1 = *(const float4*)(pk + 4);
+    const float4 v0 = *(const float4*)pv, v1 = *(const float4*)(pv + 4);
+    ak[0] += k0.x; ak[1] += k0.y; ak[2] += k0.z; ak[3] += k0.w;
+    ak[4] += k1.x; ak[5] += k1.y; ak[6] += k1.z; ak[7] += k1.w;
+    av[0] += v0.x; av[1] += v0.y; av[2] += v0.z; av[3] += v0.w;
+    av[4] += v1.x; av[5] += v1.y; av[6] += v1.z; av[7] += v1.w;
+  }
+  bf16x8 ok, ov;
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {
+    ok[x] = to_bf16(ak[x] * p.scale);
+    ov[x] = to_bf16(av[x]);
+  }
+  *(bf16x8*)(p.dk + ((size_t)bk * p.nk + kk) * D + col) = ok;
+  *(bf16x8*)(p.dv + ((size_t)bk * p.nk + kk) * D + col) = ov;
 }
 
 // ----------------------------------------------------------------- dq ----
@@ -824,7 +898,12 @@ hipError_t launch_all(const BwdParams& p, hipStream_t stream) {
                      dim3((unsigned)(((p.tc + 3) / 4) * per)), dim3(512), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_kv_kernel<D, kTest, kStats>), dim3((unsigned)(p.tc * per)),
+  hipLaunchKernelGGL((bwd_kv_kernel<D, kTest, kStats>),
+                     dim3((unsigned)((long long)p.tc * per * kSegMax)), dim3(256), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long long nfin = (long long)p.tc * per * 64 * D / 8;
+  hipLaunchKernelGGL((bwd_kv_finalize_kernel<D>), dim3((unsigned)((nfin + 255) / 256)),
                      dim3(256), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -843,12 +922,14 @@ hipError_t launch_d(const BwdParams& p, bool test, hipStream_t stream) {
 
 }  // namespace
 
-size_t bwd_workspace_bytes(int batch, int heads_q, int nq, int nk, int causal) {
+size_t bwd_workspace_bytes(int batch, int heads_q, int heads_kv, int nq, int nk, int head_dim,
+                           int causal) {
   const size_t tr = (size_t)(nq + 63) / 64, tc = (size_t)(nk + 63) / 64;
   const size_t rowinfo = (size_t)batch * heads_q * tr * kRowInfo * sizeof(float);
   const size_t per_head = causal ? tr * (tr + 1) / 2 : tr * tc;
   const size_t dmap = (size_t)batch * heads_q * per_head;
-  return ((rowinfo + 255) & ~(size_t)255) + ((dmap + 255) & ~(size_t)255);
+  const size_t part = (size_t)batch * heads_kv * tc * kSegMax * 2 * 64 * head_dim * sizeof(float);
+  return ((rowinfo + 255) & ~(size_t)255) + ((dmap + 255) & ~(size_t)255) + part;
 }
 
 hipError_t launch_bwd(const BwdArgs& a, bool test, hipStream_t stream) {
@@ -879,6 +960,8 @@ hipError_t launch_bwd(const BwdArgs& a, bool test, hipStream_t stream) {
   const size_t rowinfo = (size_t)a.batch * a.heads_q * (size_t)p.tr * kRowInfo * sizeof(float);
   p.rowinfo = (float*)a.workspace;
   p.dmap = (uint8_t*)a.workspace + ((rowinfo + 255) & ~(size_t)255);
+  const size_t dmap_bytes = (size_t)a.batch * a.heads_q * (size_t)p.dmap_per_head;
+  p.part = (float*)(p.dmap + ((dmap_bytes + 255) & ~(size_t)255));
   if (p.group % 4 == 0) {
     p.hpw = 4;
     p.ipw = 1;

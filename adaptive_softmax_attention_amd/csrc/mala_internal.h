@@ -62,7 +62,8 @@ hipError_t launch_fwd(const FwdArgs& a, bool test, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, bool test, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, bool test, hipStream_t stream);
 
-size_t bwd_workspace_bytes(int batch, int heads_q, int nq, int nk, int causal);
+size_t bwd_workspace_bytes(int batch, int heads_q, int heads_kv, int nq, int nk, int head_dim,
+                           int causal);
 size_t decode_workspace_bytes(int batch, int heads_q, int num_splits, int head_dim);
 
 }  // namespace mala

@@ -114,8 +114,10 @@ int fullattn_fwd(const mala_shape* shape, const mala_config* cfg, const void* q,
 
 /* Bytes of device workspace mala_bwd / fullattn_bwd need: fp32 row terms
  * per 64-row query block (z = LSE in log2 units, the test threshold and
- * D = rowsum(O o dO); 1 KiB per block) and one decision byte per legal tile
- * (the lower triangle when causal). Returns 0 for an invalid shape or
+ * D = rowsum(O o dO); 1 KiB per block), one decision byte per legal tile
+ * (the lower triangle when causal), and fp32 partial dK/dV sums for up to 8
+ * segments per 64-key block (8 x 2 x 64 x head_dim x 4 bytes per key block
+ * and KV head: 512 KiB at head_dim 128). Returns 0 for an invalid shape or
  * config. */
 size_t mala_bwd_workspace_bytes(const mala_shape* shape, const mala_config* cfg);
 
