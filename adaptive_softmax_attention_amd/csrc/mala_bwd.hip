@@ -67,6 +67,7 @@ struct BwdParams {
   float* rowinfo;  // [B*Hq*Tr][kRowInfo]
   uint8_t* dmap;   // backward decisions, see dmap_index()
   float* part;     // [B*Hkv*Tc][kSegMax][2][64][D] fp32 partial dK, dV
+  int seg_max;     // segments per key block at most: kSegMax (MALA) or 1 (dense)
   int batch, heads_q, heads_kv, nq, nk, group;
   int causal;
   float scale;
@@ -89,7 +90,7 @@ __device__ __forceinline__ long long dmap_index(const BwdParams& p, int bh, int 
 // Segments of key block j's items (see kSegItems).
 __device__ __forceinline__ int kv_segments(const BwdParams& p, int j) {
   const int n = p.group * (p.tr - (p.causal ? j : 0));
-  return min(kSegMax, (n + kSegItems - 1) / kSegItems);
+  return min(p.seg_max, (n + kSegItems - 1) / kSegItems);
 }
 
 // MFMA row R of subtile x holds row 32(x/2) + 8(R/4) + 4(x%2) + R%4 of the
@@ -157,7 +158,8 @@ __global__ __launch_bounds__(512, 1) void bwd_score_kernel(BwdParams p) {
   constexpr int KCH = D / 8;
   constexpr int TB = 64 * D * 2;         // bytes of a 64-row tile
   constexpr int RB = kRowInfo * 4;       // bytes of a block's row terms
-  constexpr int CPW = TB / 16 / NT;      // 16-byte copies per lane per tile
+  constexpr int CW = 4;                  // waves 4..7 issue the copies (one per SIMD)
+  constexpr int CPW = TB / 16 / (64 * CW);  // 16-byte copies per copying lane per tile
   constexpr int PF = 4;                  // Q tiles in flight (items)
   constexpr int RQ = PF + 1;             // ring: PF in flight + the one in use
   constexpr int SQ = TB + RB;
@@ -209,31 +211,36 @@ __global__ __launch_bounds__(512, 1) void bwd_score_kernel(BwdParams p) {
     }
   };
 
+  // the copying waves (w >= 4, wave index cw = w - 4) move a quarter of a
+  // tile and of the row terms each: CPW + 1 copies per wave per tile; the
+  // other wave on each SIMD keeps computing meanwhile
+  const int cw = w - CW;
   uint32_t toff[CPW];
 #pragma unroll
   for (int x = 0; x < CPW; ++x) {
-    const int s = (8 * x + w) * 64 + lane;
+    const int s = (CW * x + (cw & 3)) * 64 + lane;
     const int row = s / KCH, pc = s % KCH;
     toff[x] = (uint32_t)(row * D * 2 + ((pc ^ dsw(row)) & (KCH - 1)) * 16);
   }
   auto fetch = [&](int h, int i, char* slot) {
+    if (cw < 0) return;
     const __bf16* rows0 = p.q + (size_t)(b * p.heads_q + h) * p.nq * D;
     if (64 * i + 64 <= p.nq) {
       const char* src = (const char*)(rows0 + (size_t)64 * i * D);
 #pragma unroll
-      for (int x = 0; x < CPW; ++x) async_copy16_so(src, toff[x], slot + (8 * x + w) * 1024);
+      for (int x = 0; x < CPW; ++x) async_copy16_so(src, toff[x], slot + (CW * x + cw) * 1024);
     } else {  // ragged last block: rows past the end re-read the last row
 #pragma unroll
       for (int x = 0; x < CPW; ++x) {
-        const int s = (8 * x + w) * 64 + lane;
+        const int s = (CW * x + cw) * 64 + lane;
         const int row = s / KCH, pc = s % KCH;
         const int qq = min(64 * i + row, p.nq - 1);
         async_copy16(rows0 + (size_t)qq * D + ((pc ^ dsw(row)) & (KCH - 1)) * 8,
-                     slot + (8 * x + w) * 1024);
+                     slot + (CW * x + cw) * 1024);
       }
     }
     const float* ri = p.rowinfo + ((size_t)(b * p.heads_q + h) * p.tr + i) * kRowInfo;
-    if (lane < 8) async_copy16_so(ri, (uint32_t)(128 * w + 16 * lane), slot + TB + 128 * w);
+    if (lane < 16) async_copy16_so(ri, (uint32_t)(256 * cw + 16 * lane), slot + TB + 256 * cw);
   };
 
   for (int c0 = 0; c0 < n_items; c0 += CH) {
@@ -271,21 +278,24 @@ __global__ __launch_bounds__(512, 1) void bwd_score_kernel(BwdParams p) {
           s[qs][0] = floatx4{0.f, 0.f, 0.f, 0.f};
           s[qs][1] = floatx4{0.f, 0.f, 0.f, 0.f};
         }
+        // all 16 A operands are read up front, then the 32 products
+        bf16x8 av[NDC][4];
 #pragma unroll
-        for (int dc = 0; dc < NDC; ++dc) {
-          bf16x8 av[4];
+        for (int dc = 0; dc < NDC; ++dc)
 #pragma unroll
           for (int qs = 0; qs < 4; ++qs) {
             const int row = qperm(qs, l16);
             const int ch = 4 * dc + g4;
-            av[qs] = *(const bf16x8*)(qt + row * D * 2 + ((ch ^ dsw(row)) & (KCH - 1)) * 16);
+            av[dc][qs] = *(const bf16x8*)(qt + row * D * 2 + ((ch ^ dsw(row)) & (KCH - 1)) * 16);
           }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int dc = 0; dc < NDC; ++dc)
 #pragma unroll
           for (int qs = 0; qs < 4; ++qs) {
-            s[qs][0] = mfma16x16x32(av[qs], kreg[0][dc], s[qs][0]);
-            s[qs][1] = mfma16x16x32(av[qs], kreg[1][dc], s[qs][1]);
+            s[qs][0] = mfma16x16x32(av[dc][qs], kreg[0][dc], s[qs][0]);
+            s[qs][1] = mfma16x16x32(av[dc][qs], kreg[1][dc], s[qs][1]);
           }
-        }
         if ((p.causal && i == jw) || (64 * jw + 64 > p.nk)) {
 #pragma unroll
           for (int qs = 0; qs < 4; ++qs)
@@ -350,6 +360,17 @@ __global__ __launch_bounds__(512, 1) void bwd_score_kernel(BwdParams p) {
   }
 }
 
+// Dense path without instrumentation: every legal tile is kept, so the
+// decision map is filled with ones instead of scoring.
+__global__ __launch_bounds__(256) void bwd_dense_map_kernel(uint8_t* dmap, long long n) {
+  const long long t = ((long long)blockIdx.x * 256 + threadIdx.x) * 16;
+  if (t + 16 <= n) {
+    *(uint4*)(dmap + t) = make_uint4(0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u);
+  } else {
+    for (long long x = t; x < n; ++x) dmap[x] = 1;
+  }
+}
+
 // ----------------------------------------------------------------- kv ----
 // dK, dV over the kept tiles. A workgroup of 4 wave64s owns one key block
 // (16 keys per wave; K and V as B operands, dK and dV accumulated in
@@ -381,11 +402,14 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdParams p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l16 = lane & 15, g4 = lane >> 4;
 
-  // ---- work item: segment seg of key block j of (b, kvh), longest first ----
+  // ---- work item: segment seg of key block j of (b, kvh), longest blocks
+  //      first. (The dense path keeps one segment per block: its cost per
+  //      block is fixed, and whole blocks read the query blocks in the same
+  //      order, which the L2 shares between concurrent workgroups.) ----
   const int per = p.batch * p.heads_kv;
-  const int seg = (int)(blockIdx.x % kSegMax);
-  const int j = (int)(blockIdx.x / kSegMax / per);
-  const int bk = (int)(blockIdx.x / kSegMax % per);
+  const int seg = (int)(blockIdx.x % p.seg_max);
+  const int j = (int)(blockIdx.x / p.seg_max / per);
+  const int bk = (int)(blockIdx.x / p.seg_max % per);
   const int b = bk / p.heads_kv, kvh = bk % p.heads_kv;
   const int nseg = kv_segments(p, j);
   if (seg >= nseg) return;  // (whole workgroup, before any barrier)
@@ -894,19 +918,29 @@ hipError_t launch_all(const BwdParams& p, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long per = (long long)p.batch * p.heads_kv;
-  hipLaunchKernelGGL((bwd_score_kernel<D, kTest, kStats>),
-                     dim3((unsigned)(((p.tc + 3) / 4) * per)), dim3(512), 0, stream, p);
+  if (kTest || kStats) {
+    hipLaunchKernelGGL((bwd_score_kernel<D, kTest, kStats>),
+                       dim3((unsigned)(((p.tc + 3) / 4) * per)), dim3(512), 0, stream, p);
+  } else {
+    const long long n = (long long)p.batch * p.heads_q * p.dmap_per_head;
+    hipLaunchKernelGGL(bwd_dense_map_kernel, dim3((unsigned)((n + 4095) / 4096)), dim3(256), 0,
+                       stream, p.dmap, n);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  BwdParams q = p;
+  q.seg_max = kTest ? kSegMax : 1;
   hipLaunchKernelGGL((bwd_kv_kernel<D, kTest, kStats>),
-                     dim3((unsigned)((long long)p.tc * per * kSegMax)), dim3(256), 0, stream, p);
+                     dim3((unsigned)((long long)p.tc * per * q.seg_max)), dim3(256), 0, stream, q);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const long long nfin = (long long)p.tc * per * 64 * D / 8;
-  hipLaunchKernelGGL((bwd_kv_finalize_kernel<D>), dim3((unsigned)((nfin + 255) / 256)),
-                     dim3(256), 0, stream, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (kTest) {
+    const long long nfin = (long long)p.tc * per * 64 * D / 8;
+    hipLaunchKernelGGL((bwd_kv_finalize_kernel<D>), dim3((unsigned)((nfin + 255) / 256)),
+                       dim3(256), 0, stream, q);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const long long nblocks = (long long)p.n_ig * p.batch * p.heads_kv * p.n_hg;
   hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)nblocks), dim3(512), 0, stream, p);
   return hipGetLastError();
