@@ -686,7 +686,7 @@ __global__ __launch_bounds__(256) void bwd_kv_finalize_kernel(BwdParams p) {
 }
 
 // ----------------------------------------------------------------- dq ----
-template <int D>
+template <int D, bool kTest>  // (kTest only names the MALA / dense instances apart)
 __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
   constexpr int NDC = D / 32;
   constexpr int NDS = D / 16;
@@ -942,7 +942,7 @@ hipError_t launch_all(const BwdParams& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   const long long nblocks = (long long)p.n_ig * p.batch * p.heads_kv * p.n_hg;
-  hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)nblocks), dim3(512), 0, stream, p);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, kTest>), dim3((unsigned)nblocks), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 

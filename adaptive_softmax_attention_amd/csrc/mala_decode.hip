@@ -44,7 +44,7 @@ struct DecParams {
   uint8_t* decisions;
 };
 
-template <int D, int GM, bool kTest>
+template <int D, int GM, bool kTest, bool kStats>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecParams p) {
   constexpr int NDC = D / 32;   // reduction chunks of d for the score MFMA
   constexpr int DG = D / 8;     // 8-column groups of d (P V lanes)
@@ -121,18 +121,18 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecParams p) {
         want = col_ok;
       }
       if (col_ok && g4 == 0) {
-        if (p.counters) {
+        if (kStats && p.counters) {
           atomicAdd(&p.counters[0], 1ull);
           if (want) {
             atomicAdd(&p.counters[1], 1ull);
             atomicAdd(&p.counters[2], 64ull);
           }
         }
-        if (p.decisions)
+        if (kStats && p.decisions)
           p.decisions[(size_t)(b * p.heads_q + h0 + l16) * p.tc + j] = want ? 1 : 0;
       }
       if (!wave_any(want)) continue;  // no head retains: V tile never read
-      if (lane == 0 && p.counters) atomicAdd(&p.counters[3], 1ull);
+      if (kStats && lane == 0 && p.counters) atomicAdd(&p.counters[3], 1ull);
 
       bf16x8 vr[KT];
 #pragma unroll
@@ -244,10 +244,15 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecParams p) {
 template <int D, int GM>
 hipError_t launch_d(const DecParams& p, bool test, hipStream_t stream) {
   dim3 grid((unsigned)(p.batch * p.heads_kv * p.splits)), block(64);
-  if (test)
-    hipLaunchKernelGGL((decode_split_kernel<D, GM, true>), grid, block, 0, stream, p);
+  const bool st = p.counters != nullptr || p.decisions != nullptr;
+  if (test && st)
+    hipLaunchKernelGGL((decode_split_kernel<D, GM, true, true>), grid, block, 0, stream, p);
+  else if (test)
+    hipLaunchKernelGGL((decode_split_kernel<D, GM, true, false>), grid, block, 0, stream, p);
+  else if (st)
+    hipLaunchKernelGGL((decode_split_kernel<D, GM, false, true>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((decode_split_kernel<D, GM, false>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_split_kernel<D, GM, false, false>), grid, block, 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(p.batch * p.heads_q), dim3(D), 0, stream, p);

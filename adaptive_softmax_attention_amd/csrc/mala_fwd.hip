@@ -50,7 +50,7 @@ struct FwdParams {
   uint8_t* decisions;
 };
 
-template <int D, bool kTest>
+template <int D, bool kTest, bool kStats>
 __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   constexpr int NDC = D / 32;         // 32-wide reduction chunks over d
   constexpr int NDS = D / 16;         // 16-row subtiles of O^T over d
@@ -259,14 +259,14 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int x = 0; x < 8; ++x) anyf |= flags[x];
     if (part && half == 0 && lane == 0) {
-      if (p.counters) {
+      if (kStats && p.counters) {
         atomicAdd(&p.counters[0], 1ull);
         if (retain) {
           atomicAdd(&p.counters[1], 1ull);
           atomicAdd(&p.counters[2], (unsigned long long)vrows * 64ull);
         }
       }
-      if (p.decisions)
+      if (kStats && p.decisions)
         p.decisions[((size_t)(b * p.heads_q + h) * p.tr + i) * p.tc + j] = retain ? 1 : 0;
     }
     // the previous tile's P V (its V arrived during this tile's scoring)
@@ -275,7 +275,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
     // touch V), then K two tiles ahead
     if (anyf) {
       issue_tile(vbase, j, v_ring[j % RV], true);
-      if (tid == 0 && p.counters) atomicAdd(&p.counters[3], 1ull);
+      if (kStats && tid == 0 && p.counters) atomicAdd(&p.counters[3], 1ull);
     }
     if (j >= 2) issue_tile(kbase, j - 2, k_ring[(j - 2) % RK], false);
     v_prev = anyf != 0;
@@ -378,16 +378,27 @@ hipError_t launch_fwd(const FwdArgs& a, bool test, hipStream_t stream) {
   p.decisions = a.decisions;
   const long long nblocks = (long long)p.n_ig * p.batch * p.heads_kv * p.n_hg;
   dim3 grid((unsigned)nblocks), block(512);
+  // the instrumented variant is a separate instantiation, so the timed
+  // kernel carries no counter code
+  const bool st = p.counters != nullptr || p.decisions != nullptr;
   if (a.head_dim == 128) {
-    if (test)
-      hipLaunchKernelGGL((fwd_kernel<128, true>), grid, block, 0, stream, p);
+    if (test && st)
+      hipLaunchKernelGGL((fwd_kernel<128, true, true>), grid, block, 0, stream, p);
+    else if (test)
+      hipLaunchKernelGGL((fwd_kernel<128, true, false>), grid, block, 0, stream, p);
+    else if (st)
+      hipLaunchKernelGGL((fwd_kernel<128, false, true>), grid, block, 0, stream, p);
     else
-      hipLaunchKernelGGL((fwd_kernel<128, false>), grid, block, 0, stream, p);
+      hipLaunchKernelGGL((fwd_kernel<128, false, false>), grid, block, 0, stream, p);
   } else {
-    if (test)
-      hipLaunchKernelGGL((fwd_kernel<64, true>), grid, block, 0, stream, p);
+    if (test && st)
+      hipLaunchKernelGGL((fwd_kernel<64, true, true>), grid, block, 0, stream, p);
+    else if (test)
+      hipLaunchKernelGGL((fwd_kernel<64, true, false>), grid, block, 0, stream, p);
+    else if (st)
+      hipLaunchKernelGGL((fwd_kernel<64, false, true>), grid, block, 0, stream, p);
     else
-      hipLaunchKernelGGL((fwd_kernel<64, false>), grid, block, 0, stream, p);
+      hipLaunchKernelGGL((fwd_kernel<64, false, false>), grid, block, 0, stream, p);
   }
   return hipGetLastError();
 }
