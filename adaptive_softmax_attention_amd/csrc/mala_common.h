@@ -26,6 +26,33 @@ __device__ __forceinline__ floatx4 mfma16x16x32(const bf16x8& a, const bf16x8& b
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// v_mfma_f32_32x32x16_bf16: D(32x32, fp32) += A(32x16) * B(16x32). Lane l
+// supplies row (A) or column (B) l % 32 with reduction indices
+// 8(l/32) .. 8(l/32)+7, and receives column l % 32 of D in 16 registers:
+// register 4i + r holds row 8i + 4(l/32) + r. One wave reaches close to the
+// matrix-core peak with this shape on its own (the 16x16x32 shape needs two
+// waves per SIMD for that), and it leaves room for independent vector work
+// between consecutive products.
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16;
+__device__ __forceinline__ floatx16 mfma32x32x16(const bf16x8& a, const bf16x8& b,
+                                                 const floatx16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Maximum / sum of x over the lane pair (l, l ^ 32), which hold the two
+// 16-row halves of one column of a 32x32 MFMA result. v_permlane32_swap
+// exchanges the two 32-lane halves between its operands, so both returned
+// values are the pair seen from either side; a symmetric reduction of the
+// two is correct whichever half ends up in which.
+__device__ __forceinline__ float pair32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
@@ -108,6 +135,27 @@ __device__ __forceinline__ void async_copy16_so(const void* sbase, uint32_t voff
   // readfirstlane returns a signed int: go through uint32_t so that the low
   // half is zero-extended (a sign-extended low half would corrupt the high
   // half of the address)
+  const uint64_t a = (uint64_t)(uintptr_t)sbase;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(sb), "s"(lds)
+      : "memory", "m0");
+}
+
+// LDS byte address of a __shared__ object (a 32-bit constant for the
+// compiler; no generic-pointer arithmetic or null checks).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
+}
+// async_copy16_so with the LDS destination given as a byte address.
+__device__ __forceinline__ void async_copy16_sa(const void* sbase, uint32_t voff, uint32_t lds_byte) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_byte);
   const uint64_t a = (uint64_t)(uintptr_t)sbase;
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
@@ -223,6 +271,24 @@ __device__ __forceinline__ int tr_swz(int row) { return (row << 1) ^ ((row >> 3)
 // row bits 3 ^ 4 (distinct for the 8- and 16-row groups of the row-major
 // reads); with 256-byte rows (d = 128) both access kinds are free of bank
 // conflicts for 32 or 64 four-byte banks.
+// Tiles of the 32x32 products ([64 rows][D] bf16, 16-byte chunks XORed per
+// row). K-type tiles are read row-major by 32 consecutive rows per
+// instruction (one chunk each); their swizzle makes any 16 consecutive rows
+// hit distinct 16-byte bank groups. V-type tiles are read with the
+// transposing read, 4 consecutive rows x 16 columns per 16-lane group and 4
+// chunks across a 32-lane phase; their swizzle keeps those 4 rows on distinct
+// bank groups for 32- and 64-bank phases.
+template <int D>
+__device__ __forceinline__ int kswz32(int row) {
+  if constexpr (D == 128) return row & 15;
+  else return (row & 7) ^ ((row >> 3) & 1);
+}
+template <int D>
+__device__ __forceinline__ int vswz32(int row) {
+  if constexpr (D == 128) return (6 * (row & 1)) ^ (10 * ((row >> 1) & 1));
+  else return 2 * (row & 3);
+}
+
 __device__ __forceinline__ int dsw(int row) {
   return (((row >> 3) ^ (row >> 4)) & 1) | ((row & 3) << 1) | (((row >> 3) & 1) << 3);
 }

@@ -5,26 +5,28 @@
 //
 // Work decomposition (gfx950):
 //   * a pair of wave64s owns one 64-row decision block (query block i of
-//     head h), 32 rows each; each wave ballots its rows and the pair's two
-//     bits are combined through LDS at the barrier that already separates
-//     score discovery from the V load, so the test of Eq. 3 costs no extra
-//     synchronisation;
-//   * a workgroup of 8 waves holds 4 blocks that share K/V tiles: 4 query
-//     heads of one KV head (GQA), or 2 heads x 2 blocks, or 4 consecutive
-//     query blocks of one head;
-//   * scores are formed transposed, S^T = K Q^T (16x16x32 bf16 MFMA, fp32
-//     accumulate), so each lane holds 16 keys of one query column: the row
-//     max and row sum need only 2 cross-lane steps, and P^T is already in
-//     the B-operand layout of O^T = V^T P^T;
+//     head h), 32 rows each, two waves per SIMD; a workgroup of 8 waves holds
+//     4 blocks that share K/V tiles: 4 query heads of one KV head (GQA), or
+//     2 heads x 2 blocks, or 4 consecutive query blocks of one head;
+//   * scores are formed transposed, S^T = K Q^T, on 32x32x16 bf16 MFMA with
+//     fp32 accumulation: each lane holds 32 keys of one query column, so
+//     the row max and sum need one lane-pair exchange, and P^T is already
+//     in the B-operand layout of O^T = V^T P^T;
+//   * the two halves of a block agree on the test of Eq. 3 through tagged
+//     words in LDS (each publishes its ballot and waits for the other's on
+//     the same tile), so the softmax of a tile runs in the iteration that
+//     scored it;
 //   * K and V tiles are copied asynchronously from global memory straight
-//     into LDS rings (global_load_lds, row-major, swizzled); V^T operands are
-//     read with the transposing LDS read, so nothing is staged in registers;
+//     into LDS rings (global_load_lds, row-major, XOR-swizzled per row);
+//     V^T operands are read with the transposing LDS read;
 //   * software pipeline over the key blocks, visited from the diagonal down
-//     (Sec. 2.2): K runs two tiles ahead; a tile's V is requested only after
-//     the ballot says some block retains it, and is consumed one iteration
-//     later: the running (m, l) update of a tile needs only its scores, so
-//     the next tile's score discovery proceeds while V is in flight, and
-//     O <- alpha O + P V is applied a step late in the same order;
+//     (Sec. 2.2), one barrier per tile: K runs two tiles ahead; a tile's V is
+//     requested at the barrier after every block's decision on it is known,
+//     and O <- alpha O + P V of that tile runs one iteration later, inside
+//     the same basic block as the next tile's softmax so that the products
+//     and the exponentials overlap;
+//   * exponentials use a reference maximum that moves only on jumps of more
+//     than 8 (log2 units), which makes the O rescale rare;
 //   * workgroups are issued longest-first (largest query block first).
 #include "mala_common.h"
 #include "mala_internal.h"
@@ -52,21 +54,26 @@ struct FwdParams {
 
 template <int D, bool kTest, bool kStats>
 __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
-  constexpr int NDC = D / 32;         // 32-wide reduction chunks over d
-  constexpr int NDS = D / 16;         // 16-row subtiles of O^T over d
+  constexpr int NDC = D / 16;         // 16-wide reduction chunks over d
+  constexpr int NDT = D / 32;         // 32-row subtiles of O^T over d
   constexpr int KCH = D / 8;          // 16-byte chunks per K / V row
-  constexpr int NT = 512;             // threads per workgroup
-  constexpr int NQS = 2;              // 16-query subtiles per wave (32 rows)
+  constexpr int NT = 512;             // threads per workgroup (8 waves)
   constexpr int CPT = 64 * KCH / NT;  // async 16-byte copies per thread per tile
   constexpr int RK = 3;               // K ring: current tile + 2 ahead
   constexpr int RV = 2;               // V ring
+  constexpr uint32_t kTileBytes = 64 * D * 2;
+  // The exponentials are taken against a reference maximum that moves only
+  // when a tile's row maximum exceeds it by more than this (log2 units), so
+  // P <= 2^8 and the O rescale is rare; m + log2(l) is the same either way.
+  constexpr float kLazy = 8.f;
 
   __shared__ __attribute__((aligned(16))) __bf16 k_ring[RK][64 * D];
   __shared__ __attribute__((aligned(16))) __bf16 v_ring[RV][64 * D];
-  __shared__ int flags[8];
+  __shared__ int vflags[2][8];  // block decisions, read after the next barrier
+  __shared__ int pflags[8];     // row-half ballots, tagged with the tile
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int l16 = lane & 15, g4 = lane >> 4;
+  const int l32 = lane & 31, hh = lane >> 5;
 
   // ---- work item (longest query-block group first) ----
   const int per_ig = p.batch * p.heads_kv * p.n_hg;
@@ -81,264 +88,270 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   const int h = kvh * p.group + hg * p.hpw + (blk % p.hpw);
   const int i = ig * p.ipw + (blk / p.hpw);
   const bool valid = i < p.tr;
-  const int q0 = i * 64 + 32 * half;  // first row of this wave
-  const int bq0 = i * 64;             // first row of the block
+  const int qq = i * 64 + 32 * half + l32;  // the query column this lane holds
   const int jmax = valid ? (p.causal ? i : p.tc - 1) : -1;
   const int i_top = min(ig * p.ipw + p.ipw - 1, p.tr - 1);
   const int jtop = p.causal ? i_top : p.tc - 1;
-  const int vrows = valid ? min(64, p.nq - bq0) : 0;
+  const int vrows = valid ? min(64, p.nq - i * 64) : 0;
 
   const size_t qrow0 = (size_t)(b * p.heads_q + h) * p.nq;
   const __bf16* kbase = p.k + (size_t)(b * p.heads_kv + kvh) * p.nk * D;
   const __bf16* vbase = p.v + (size_t)(b * p.heads_kv + kvh) * p.nk * D;
 
-  // ---- Q block in registers: B operand of S^T = K Q^T ----
-  bf16x8 qr[NQS][NDC];
-#pragma unroll
-  for (int qs = 0; qs < NQS; ++qs) {
-    const int qq = q0 + 16 * qs + l16;
-#pragma unroll
-    for (int dc = 0; dc < NDC; ++dc) {
-      if (valid && qq < p.nq)
-        qr[qs][dc] = *(const bf16x8*)(p.q + (qrow0 + qq) * D + 32 * dc + 8 * g4);
-      else
-        qr[qs][dc] = bf16x8{};
-    }
-  }
+  const bool row_ok = valid && qq < p.nq;
+  const float L = p.causal ? (float)(qq + 1) : (float)p.nk;  // visible keys
+  const float thr = p.log2_tau - log2f(L);                    // log2(tau / L_q)
+  float mref = -INFINITY, lsum = 0.f;
 
-  // ---- running state per query column of this lane ----
-  float m2[NQS], lsum[NQS], thr[NQS];
-  floatx4 oacc[NDS][NQS];
+  // ---- Q^T in registers: B operand of S^T = K Q^T ----
+  bf16x8 qr[NDC];
 #pragma unroll
-  for (int qs = 0; qs < NQS; ++qs) {
-    const int qq = q0 + 16 * qs + l16;
-    m2[qs] = -INFINITY;
-    lsum[qs] = 0.f;
-    const float L = p.causal ? (float)(qq + 1) : (float)p.nk;  // visible keys
-    thr[qs] = p.log2_tau - log2f(L);                            // log2(tau / L_q)
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) oacc[ds][qs] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int dc = 0; dc < NDC; ++dc) {
+    bf16x8 t = bf16x8{};
+    if (row_ok) t = *(const bf16x8*)(p.q + (qrow0 + qq) * D + 16 * dc + 8 * hh);
+    qr[dc] = t;
   }
+  // the Q loads are the only loads the compiler tracks; retire them here so
+  // that no wait for them lands inside the pipelined loop
+  vmcnt_wait<0>();
+  if (tid < 8) pflags[tid] = 0;
+
+  floatx16 oacc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[dt][e] = 0.f;
 
   // ---- async tile copies (rows past the end re-read the last row; those
   //      keys are masked, so only finite values reach the products) ----
-  auto issue_tile = [&](const __bf16* base, int j, __bf16* slot, bool tr_layout) {
+  const uint32_t k_lds = lds_addr(&k_ring[0][0]), v_lds = lds_addr(&v_ring[0][0]);
+  auto issue_tile = [&](const __bf16* base, int j, uint32_t slot_lds, bool vtype) {
+    const __bf16* tb = base + (size_t)j * 64 * D;  // wave-uniform tile base
+    const int last = p.nk - 1 - j * 64;              // last row inside the keys
 #pragma unroll
     for (int x = 0; x < CPT; ++x) {
       const int s0 = x * NT + w * 64;  // first 16-byte slot of this wave
       const int s = s0 + lane;
       const int row = s / KCH, pc = s % KCH;
-      const int sw = tr_layout ? (tr_swz(row) & (KCH - 1)) : (k_swz(row) & (KCH - 1));
-      const int key = min(j * 64 + row, p.nk - 1);
-      async_copy16(base + (size_t)key * D + (pc ^ sw) * 8, slot + s0 * 8);
+      const int sw = vtype ? vswz32<D>(row) : kswz32<D>(row);
+      const uint32_t voff = (uint32_t)((min(row, last) * D + ((pc ^ sw) & (KCH - 1)) * 8) * 2);
+      async_copy16_sa(tb, voff, slot_lds + (uint32_t)s0 * 16u);
     }
   };
 
-  // pending post-score work of the previous tile (applied one step late)
-  bool pend = false;
-  bf16x8 pend_pb[2][NQS];
-  float pend_alpha[NQS];
-  bool v_prev = false;  // V of the previous tile was requested
-
-  auto apply_pv = [&](const __bf16* vt) {
-    // O^T <- alpha O^T + V^T P^T
+  // ---- the pieces of one pipeline step ----
+  // S^T of tile j: subtile kt holds keys 32kt + 8e' + 4hh + r (register
+  // 4e' + r) of this lane's query column
+  auto score = [&](const __bf16* kt_lds, floatx16 (&s)[2]) {
 #pragma unroll
-    for (int qs = 0; qs < NQS; ++qs)
+    for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
-        oacc[ds][qs][0] *= pend_alpha[qs];
-        oacc[ds][qs][1] *= pend_alpha[qs];
-        oacc[ds][qs][2] *= pend_alpha[qs];
-        oacc[ds][qs][3] *= pend_alpha[qs];
-      }
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
-        // lane addresses row k0 + l16/4, columns 16ds + 4(l16%4): the
-        // transposing read returns V[k0 + e][16ds + l16], e = 0..3
-        short4v t[2];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int row = 32 * kc + 8 * g4 + 4 * hh + (l16 >> 2);
-          const int col = 16 * ds + 4 * (l16 & 3);
-          const int ch = col >> 3;
-          t[hh] = lds_read_tr4(vt + row * D + ((ch ^ (tr_swz(row) & (KCH - 1))) * 8) + (col & 7));
-        }
-        const bf16x8 a = join_tr(t[0], t[1]);
-#pragma unroll
-        for (int qs = 0; qs < NQS; ++qs)
-          oacc[ds][qs] = mfma16x16x32(a, pend_pb[kc][qs], oacc[ds][qs]);
-      }
-  };
-
-  // prologue: K of the first two tiles
-  issue_tile(kbase, jtop, k_ring[jtop % RK], false);
-  if (jtop >= 1) issue_tile(kbase, jtop - 1, k_ring[(jtop - 1) % RK], false);
-
-  for (int j = jtop; j >= 0; --j) {
-    // K_j complete; V_{j+1} and K_{j-1} may still be in flight
-    vmcnt_wait_le((v_prev ? CPT : 0) + (j >= 1 ? CPT : 0));
-    lds_barrier();
-    const __bf16* kt = k_ring[j % RK];
-
-    const bool part = valid && j <= jmax;
-    bool want = false;
-    floatx4 s[4][NQS];
-    float mt[NQS];
-    if (part) {
-      // score discovery, every legal tile
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int qs = 0; qs < NQS; ++qs) s[ks][qs] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int e = 0; e < 16; ++e) s[kt][e] = 0.f;
+      const int row = 32 * kt + l32;
 #pragma unroll
       for (int dc = 0; dc < NDC; ++dc) {
+        const int ch = ((2 * dc + hh) ^ kswz32<D>(row)) & (KCH - 1);
+        const bf16x8 a = *(const bf16x8*)(kt_lds + row * D + ch * 8);
+        s[kt] = mfma32x32x16(a, qr[dc], s[kt]);
+      }
+    }
+  };
+  // causal / ragged-tail mask of tile j: key offset o = 32kt + 8(e/4) + e%4
+  // past 4hh is legal iff o <= lim
+  auto mask = [&](floatx16 (&s)[2], int j) {
+    int lim = p.nk - 1 - j * 64 - 4 * hh;
+    if (p.causal) lim = min(lim, qq - j * 64 - 4 * hh);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          // MFMA row l16 of key subtile ks holds key 32(ks/2)+8(l16/4)+4(ks%2)+l16%4,
-          // so output lane group g4 ends up with 8 consecutive keys per 32
-          const int kr = 32 * (ks >> 1) + 8 * (l16 >> 2) + 4 * (ks & 1) + (l16 & 3);
-          const int ch = 4 * dc + g4;
-          const bf16x8 a = *(const bf16x8*)(kt + kr * D + ((ch ^ (k_swz(kr) & (KCH - 1))) * 8));
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int qs = 0; qs < NQS; ++qs) s[ks][qs] = mfma16x16x32(a, qr[qs][dc], s[ks][qs]);
+      for (int e = 0; e < 16; ++e)
+        if (32 * kt + 8 * (e >> 2) + (e & 3) > lim) s[kt][e] = -INFINITY;
+  };
+  // tile row maximum (raw units) and this row half's vote under Eq. 3 in
+  // log2 units: a row wants the tile unless rowmax*c - m - log2(l) <
+  // log2(tau/L); l = 0 counts as +inf
+  auto vote = [&](const floatx16 (&s)[2], float& mt) {
+    float x = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) x = fmaxf(x, s[kt][e]);
+    mt = pair32_max(x);
+    if constexpr (kTest) {
+      const float mg = mt * p.c - mref - fast_log2(lsum) - thr;
+      return wave_any(row_ok && mt != -INFINITY && (lsum == 0.f || !(mg < 0.f)));
+    } else {
+      return true;
+    }
+  };
+  // online-softmax update of a retained tile for every valid row: the
+  // exponentials against the reference maximum, the O rescale factor, the
+  // running sum and the bf16 P operand. For key chunk kc = 2kt + c the B
+  // operand of O^T = V^T P^T holds keys 16kc + 8(e/4) + 4hh + e%4, i.e.
+  // registers 8c .. 8c+7 of subtile kt.
+  auto softmax = [&](floatx16 (&s)[2], float mt, float& alpha, bf16x8 (&pb)[4]) {
+    const float mtc = mt * p.c;
+    const bool mv = mtc > mref + kLazy;
+    const float mnew = mv ? mtc : mref;
+    const float mu = (mnew == -INFINITY) ? 0.f : mnew;
+    alpha = mv ? fast_exp2(mref - mu) : 1.f;
+    mref = mnew;
+    float rs = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float pv = fast_exp2(s[kt][e] * p.c - mu);
+        s[kt][e] = pv;
+        rs += pv;
+      }
+    lsum = alpha * lsum + pair32_sum(rs);
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      bf16x8 t;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t[e] = to_bf16(s[kc >> 1][8 * (kc & 1) + e]);
+      pb[kc] = t;
+    }
+  };
+  // O^T += V^T P^T over one tile; the V^T operand of key chunk kc holds keys
+  // 16kc + 4hh + 0..3 and 16kc + 8 + 4hh + 0..3 of column 32dt + l32
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const int tr_row = 4 * (g16 >> 1) + (j16 >> 2);
+  const int tr_col = 16 * (g16 & 1) + 4 * (j16 & 3);
+  auto pv = [&](const __bf16* vt, const bf16x8 (&pb)[4]) {
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        short4v t[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int row = 16 * kc + 8 * u + tr_row;
+          const int col = 32 * dt + tr_col;
+          const int ch = ((col >> 3) ^ vswz32<D>(row)) & (KCH - 1);
+          t[u] = lds_read_tr4(vt + row * D + ch * 8 + (col & 7));
         }
+        oacc[dt] = mfma32x32x16(join_tr(t[0], t[1]), pb[kc], oacc[dt]);
       }
-      // causal mask at the diagonal and the ragged key tail
-      const bool need_mask = (p.causal && j == i) || (j * 64 + 63 >= p.nk);
-      if (need_mask) {
+  };
+
+  // ---- software pipeline, one barrier per key tile ----
+  // Iteration j scores and tests tile j (the two row halves of a block agree
+  // through tagged LDS words, without a barrier), then applies P V of tile
+  // j+2 (its V was requested one iteration earlier, once every block's
+  // decision on it was published at the barrier) while forming the softmax
+  // of tile j. P of tiles j and j+2 share a register set (the products read
+  // it before the softmax overwrites it); the sets alternate by tile
+  // parity, so the loop body runs twice per trip.
+  floatx16 sc[2];
+  bf16x8 pA[4], pB[4];
+  float mt = -INFINITY, alA = 1.f, alB = 1.f;
+  bool pendA = false, pendB = false;  // P V outstanding for the tile in that set
+  bool d_last = false;                // this block's decision on tile j+1
+
+  issue_tile(kbase, jtop, k_lds + (jtop % RK) * kTileBytes, false);
+  if (jtop >= 1) issue_tile(kbase, jtop - 1, k_lds + ((jtop - 1) % RK) * kTileBytes, false);
+
+  auto step = [&](int j, bf16x8 (&pset)[4], float& al, bool& pend) {
+    // K_j and V_{j+2} complete (K_{j-1} may stay in flight); decisions on
+    // tile j+1 published
+    vmcnt_wait_le(j >= 1 ? CPT : 0);
+    lds_barrier();
+    const int jn = j + 1;
+    int any1 = 0;
+    if (jn >= 0 && jn <= jtop) {
+      const int* f = vflags[jn & 1];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-          for (int qs = 0; qs < NQS; ++qs)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int key = j * 64 + 32 * (ks >> 1) + 8 * g4 + 4 * (ks & 1) + r;
-              const int qq = q0 + 16 * qs + l16;
-              if (key >= p.nk || (p.causal && key > qq)) s[ks][qs][r] = -INFINITY;
-            }
-      }
-      // tile row maxima
-#pragma unroll
-      for (int qs = 0; qs < NQS; ++qs) {
-        float x = -INFINITY;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) x = fmaxf(x, s[ks][qs][r]);
-        mt[qs] = group4_max(x);
-      }
-      if constexpr (kTest) {
-        // Eq. 3 in log2 units: skip iff every valid row with a legal key has
-        // rowmax*c - m - log2(l) < log2(tau/L); l = 0 counts as +inf
-#pragma unroll
-        for (int qs = 0; qs < NQS; ++qs) {
-          const int qq = q0 + 16 * qs + l16;
-          if (qq < p.nq && mt[qs] != -INFINITY) {
-            if (lsum[qs] == 0.f) {
-              want = true;
-            } else {
-              const float mg = mt[qs] * p.c - m2[qs] - fast_log2(lsum[qs]) - thr[qs];
-              if (!(mg < 0.f)) want = true;
-            }
+      for (int x = 0; x < 8; ++x) any1 |= f[x];
+      if (kStats && valid && jn <= jmax && half == 0 && lane == 0) {
+        if (p.counters) {
+          atomicAdd(&p.counters[0], 1ull);
+          if (d_last) {
+            atomicAdd(&p.counters[1], 1ull);
+            atomicAdd(&p.counters[2], (unsigned long long)vrows * 64ull);
           }
         }
-        want = wave_any(want);
-      } else {
-        want = true;
+        if (p.decisions)
+          p.decisions[((size_t)(b * p.heads_q + h) * p.tr + i) * p.tc + jn] = d_last ? 1 : 0;
       }
     }
-    if (lane == 0) flags[w] = want ? 1 : 0;
-    // V_{j+1} complete (K_{j-1} may stay in flight); flags visible
-    if (v_prev) vmcnt_wait_le(j >= 1 ? CPT : 0);
-    lds_barrier();
-    // block decision = either half wants it; V is needed if any block retains
-    const bool retain = part && (flags[2 * blk] | flags[2 * blk + 1]) != 0;
-    int anyf = 0;
-#pragma unroll
-    for (int x = 0; x < 8; ++x) anyf |= flags[x];
-    if (part && half == 0 && lane == 0) {
-      if (kStats && p.counters) {
-        atomicAdd(&p.counters[0], 1ull);
-        if (retain) {
-          atomicAdd(&p.counters[1], 1ull);
-          atomicAdd(&p.counters[2], (unsigned long long)vrows * 64ull);
-        }
-      }
-      if (kStats && p.decisions)
-        p.decisions[((size_t)(b * p.heads_q + h) * p.tr + i) * p.tc + j] = retain ? 1 : 0;
-    }
-    // the previous tile's P V (its V arrived during this tile's scoring)
-    if (pend) apply_pv(v_ring[(j + 1) % RV]);
-    // request V_j only if some block retains tile j (skipped tiles never
-    // touch V), then K two tiles ahead
-    if (anyf) {
-      issue_tile(vbase, j, v_ring[j % RV], true);
+    // V of tile j+1 only if some block retains it; then K two tiles ahead
+    if (any1) {
+      issue_tile(vbase, jn, v_lds + (jn % RV) * kTileBytes, true);
       if (kStats && tid == 0 && p.counters) atomicAdd(&p.counters[3], 1ull);
     }
-    if (j >= 2) issue_tile(kbase, j - 2, k_ring[(j - 2) % RK], false);
-    v_prev = anyf != 0;
+    if (j >= 2) issue_tile(kbase, j - 2, k_lds + ((j - 2) % RK) * kTileBytes, false);
 
-    pend = retain;
-    if (retain) {
-      // online-softmax update of every valid row; the
-      // O update for this tile is applied next iteration
-#pragma unroll
-      for (int qs = 0; qs < NQS; ++qs) {
-        const float mn = fmaxf(m2[qs], mt[qs] * p.c);
-        const float mu = (mn == -INFINITY) ? 0.f : mn;
-        const float alpha = fast_exp2(m2[qs] - mu);
-        float rs = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float pv = fast_exp2(s[ks][qs][r] * p.c - mu);
-            s[ks][qs][r] = pv;
-            rs += pv;
-          }
-        rs = group4_sum(rs);
-        lsum[qs] = alpha * lsum[qs] + rs;
-        m2[qs] = mn;
-        pend_alpha[qs] = alpha;
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-          bf16x8 t;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            t[r] = to_bf16(s[2 * kc][qs][r]);
-            t[4 + r] = to_bf16(s[2 * kc + 1][qs][r]);
-          }
-          pend_pb[kc][qs] = t;
-        }
+    // scores and decision of tile j
+    const bool do_s = j >= 0 && valid && j <= jmax;
+    bool dj = false;
+    if (do_s) {
+      score(&k_ring[0][0] + (j % RK) * 64 * D, sc);
+      if ((p.causal && j == i) || (j * 64 + 63 >= p.nk)) mask(sc, j);
+      const bool mine = vote(sc, mt);
+      if constexpr (kTest) {
+        // publish this half's vote tagged with the tile, then wait for the
+        // other half's vote on the same tile. Both halves take this path
+        // for the same tiles and nothing between the barrier and here
+        // waits on another wave, so the wait ends.
+        const int tag = 2 * (j + 1);
+        __hip_atomic_store(&pflags[w], tag | (mine ? 1 : 0), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
+        int other;
+        do {
+          other = __hip_atomic_load(&pflags[w ^ 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        } while ((other & ~1) != tag);
+        dj = mine || (other & 1);
+      } else {
+        dj = true;
       }
     }
+    // every lane stores the same word: no divergent branch needed
+    if (j >= 0) vflags[j & 1][w] = dj ? 1 : 0;
+    d_last = dj;
+
+    // P V of tile j+2 with the softmax of tile j
+    const bool pv_old = pend;
+    if (pv_old && wave_any(al != 1.f)) {
+      // O must be relative to the reference maximum P of tile j+2 was formed with
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[dt][e] *= al;
+    }
+    const __bf16* vt = &v_ring[0][0] + ((j + 2) % RV) * 64 * D;
+    if (pv_old && dj) {
+      pv(vt, pset);
+      softmax(sc, mt, al, pset);
+    } else if (pv_old) {
+      pv(vt, pset);
+    } else if (dj) {
+      softmax(sc, mt, al, pset);
+    }
+    pend = dj;
+  };
+
+  // j runs down to -2 to drain the pipeline
+  for (int j = jtop; j >= -2; j -= 2) {
+    step(j, pA, alA, pendA);
+    if (j - 1 >= -2) step(j - 1, pB, alB, pendB);
   }
-  // the last tile's P V
-  vmcnt_wait<0>();
-  lds_barrier();
-  if (pend) apply_pv(v_ring[0]);
 
   // ---- finalisation: O = O / l, LSE = m + log l ----
-  if (valid) {
+  if (row_ok) {
+    const float inv = 1.f / lsum;
+    __bf16* orow = p.o + (qrow0 + qq) * D;
 #pragma unroll
-    for (int qs = 0; qs < NQS; ++qs) {
-      const int qq = q0 + 16 * qs + l16;
-      if (qq >= p.nq) continue;
-      const float inv = 1.f / lsum[qs];
-      __bf16* orow = p.o + (qrow0 + qq) * D;
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
+      for (int e4 = 0; e4 < 4; ++e4) {
         bf16x4 t;
-        t[0] = to_bf16(oacc[ds][qs][0] * inv);
-        t[1] = to_bf16(oacc[ds][qs][1] * inv);
-        t[2] = to_bf16(oacc[ds][qs][2] * inv);
-        t[3] = to_bf16(oacc[ds][qs][3] * inv);
-        *(bf16x4*)(orow + 16 * ds + 4 * g4) = t;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) t[r] = to_bf16(oacc[dt][4 * e4 + r] * inv);
+        *(bf16x4*)(orow + 32 * dt + 8 * e4 + 4 * hh) = t;
       }
-      if (g4 == 0) p.lse[qrow0 + qq] = (m2[qs] + log2f(lsum[qs])) * kLn2;
-    }
+    if (hh == 0) p.lse[qrow0 + qq] = (mref + log2f(lsum)) * kLn2;
   }
 }
 
