@@ -143,197 +143,172 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 
 // -------------------------------------------------------------- score ----
 // Offline test of every legal tile (Eq. 4), key-major. A workgroup of 8
-// wave64s (two per SIMD) owns 4 key blocks (256 keys) of one KV head; wave w
-// holds 32 keys of block w/2 as MFMA B operands. It streams the Q tiles of
-// every (query block, query head) item from the last query block down,
-// through an LDS ring filled by asynchronous copies, scores them
-// (16x16x32 bf16 MFMA, 2 products per A-operand read) and compares each
-// legal score with the row threshold W_q. A block keeps the tile when any
-// of its two waves finds s >= W_q. Decisions go to the byte map read by the
-// dK/dV and dQ passes.
+// wave64s owns 4 key blocks (256 keys) of one KV head. Wave w holds all 64
+// keys of block w % 4 as the A operand of S^T = K Q^T (32x32x16 bf16 MFMA,
+// fp32 accumulation) and scores every other item: waves 0-3 the even items,
+// waves 4-7 the odd ones, so the two waves on a SIMD share a key block and
+// each decides its own tiles with no exchange. Q tiles and the per-row
+// thresholds W_q stream through an LDS ring filled by asynchronous copies
+// (PF items ahead) from the last query block down; every workgroup walks the
+// items in the same order, so concurrent workgroups find each Q tile in L2.
+// A lane holds one query column of 32 keys per subtile: its test is the
+// maximum of those scores against W_q, then one ballot. Decisions go to the
+// byte map read by the dK/dV and dQ passes.
 template <int D, bool kTest, bool kStats>
 __global__ __launch_bounds__(512, 1) void bwd_score_kernel(BwdParams p) {
   constexpr int NT = 512;
-  constexpr int NDC = D / 32;
-  constexpr int KCH = D / 8;
+  constexpr int NDC = D / 16;            // 16-wide reduction chunks over d
+  constexpr int KCH = D / 8;             // 16-byte chunks per row
   constexpr int TB = 64 * D * 2;         // bytes of a 64-row tile
-  constexpr int RB = kRowInfo * 4;       // bytes of a block's row terms
-  constexpr int CW = 4;                  // waves 4..7 issue the copies (one per SIMD)
-  constexpr int CPW = TB / 16 / (64 * CW);  // 16-byte copies per copying lane per tile
-  constexpr int PF = 4;                  // Q tiles in flight (items)
-  constexpr int RQ = PF + 1;             // ring: PF in flight + the one in use
-  constexpr int SQ = TB + RB;
+  constexpr int WB = 64 * 4;             // bytes of a block's thresholds
+  constexpr int SQ = TB + WB;            // ring slot
+  constexpr int CPW = TB / 16 / NT;      // tile copies per lane per item
+  constexpr int PF = 6;                  // items in flight
+  constexpr int RQ = PF + 2;             // + the two in use
   constexpr int NB = 4;                  // key blocks per workgroup
   constexpr int CH = 1024;               // items per chunk (decisions held in LDS)
 
   __shared__ __attribute__((aligned(16))) char ring[RQ * SQ];
   __shared__ uint8_t dec_lds[NB][CH];
-  __shared__ int flags[2][8];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int l16 = lane & 15, g4 = lane >> 4;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int xb = w & 3;   // key block of this wave within the group
+  const int par = w >> 2; // parity of the items this wave scores
 
   const int per = p.batch * p.heads_kv;
   const int G4 = (int)(blockIdx.x / per);  // key blocks 4 G4 .. 4 G4 + 3, longest first
   const int bk = (int)(blockIdx.x % per);
   const int b = bk / p.heads_kv, kvh = bk % p.heads_kv;
   const int jb0 = NB * G4;
-  const int jw = jb0 + (w >> 1);  // this wave's key block
+  const int jw = jb0 + xb;  // this wave's key block
   const __bf16* kbase = p.k + (size_t)bk * p.nk * D;
 
-  // K of this wave's 32 keys (two 16-key subtiles) as B operands
-  int key[2];
+  // K of the 64 keys as A operands: subtile kt, lane row 32 kt + l32
   bf16x8 kreg[2][NDC];
 #pragma unroll
-  for (int ns = 0; ns < 2; ++ns) {
-    key[ns] = 64 * jw + 32 * (w & 1) + 16 * ns + l16;
-    const bool ok = key[ns] < p.nk;
+  for (int kt = 0; kt < 2; ++kt) {
+    const int key = 64 * jw + 32 * kt + l32;
+    const bool ok = jw < p.tc && key < p.nk;
 #pragma unroll
     for (int dc = 0; dc < NDC; ++dc)
-      kreg[ns][dc] =
-          ok ? *(const bf16x8*)(kbase + (size_t)key[ns] * D + 32 * dc + 8 * g4) : bf16x8{};
+      kreg[kt][dc] = ok ? *(const bf16x8*)(kbase + (size_t)key * D + 16 * dc + 8 * hh) : bf16x8{};
   }
+  // retire the register loads here: the asynchronous copies below are not
+  // counted by the compiler's own waits
+  vmcnt_wait<0>();
+
   // key block x (0..3) of this workgroup has a legal entry for query block i
   auto legal = [&](int x, int i) {
     const int j = jb0 + x;
     return j < p.tc && (!p.causal || i >= j);
   };
-
   const int i_lo = p.causal ? jb0 : 0;
   const int n_items = p.group * (p.tr - i_lo);
   auto item_i = [&](int it) { return p.tr - 1 - it / p.group; };
   auto item_h = [&](int it) { return kvh * p.group + it % p.group; };
-  auto advance = [&](int& i_, int& hh_) {
-    if (++hh_ == p.group) {
-      hh_ = 0;
-      --i_;
-    }
-  };
 
-  // the copying waves (w >= 4, wave index cw = w - 4) move a quarter of a
-  // tile and of the row terms each: CPW + 1 copies per wave per tile; the
-  // other wave on each SIMD keeps computing meanwhile
-  const int cw = w - CW;
-  uint32_t toff[CPW];
-#pragma unroll
-  for (int x = 0; x < CPW; ++x) {
-    const int s = (CW * x + (cw & 3)) * 64 + lane;
-    const int row = s / KCH, pc = s % KCH;
-    toff[x] = (uint32_t)(row * D * 2 + ((pc ^ dsw(row)) & (KCH - 1)) * 16);
-  }
+  // copies of item (h, i): CPW tile chunks per lane (row-major, chunks
+  // XOR-swizzled per row as the 32-row operand reads expect) and two of the
+  // 16 threshold chunks per wave
   auto fetch = [&](int h, int i, char* slot) {
-    if (cw < 0) return;
     const __bf16* rows0 = p.q + (size_t)(b * p.heads_q + h) * p.nq * D;
-    if (64 * i + 64 <= p.nq) {
-      const char* src = (const char*)(rows0 + (size_t)64 * i * D);
+    const int last = p.nq - 1 - 64 * i;  // last row inside the queries
 #pragma unroll
-      for (int x = 0; x < CPW; ++x) async_copy16_so(src, toff[x], slot + (CW * x + cw) * 1024);
-    } else {  // ragged last block: rows past the end re-read the last row
-#pragma unroll
-      for (int x = 0; x < CPW; ++x) {
-        const int s = (CW * x + cw) * 64 + lane;
-        const int row = s / KCH, pc = s % KCH;
-        const int qq = min(64 * i + row, p.nq - 1);
-        async_copy16(rows0 + (size_t)qq * D + ((pc ^ dsw(row)) & (KCH - 1)) * 8,
-                     slot + (CW * x + cw) * 1024);
-      }
+    for (int x = 0; x < CPW; ++x) {
+      const int s0 = x * NT + w * 64;
+      const int s = s0 + lane;
+      const int row = s / KCH, pc = s % KCH;
+      const uint32_t voff =
+          (uint32_t)((min(row, last) * D + ((pc ^ kswz32<D>(row)) & (KCH - 1)) * 8) * 2);
+      async_copy16_so(rows0 + (size_t)64 * i * D, voff, slot + s0 * 16);
     }
-    const float* ri = p.rowinfo + ((size_t)(b * p.heads_q + h) * p.tr + i) * kRowInfo;
-    if (lane < 16) async_copy16_so(ri, (uint32_t)(256 * cw + 16 * lane), slot + TB + 256 * cw);
+    const float* ri = p.rowinfo + ((size_t)(b * p.heads_q + h) * p.tr + i) * kRowInfo + 64;
+    if (lane < 2) async_copy16_so(ri, (uint32_t)(16 * (2 * w + lane)), slot + TB + 32 * w);
   };
 
   for (int c0 = 0; c0 < n_items; c0 += CH) {
     const int nc = min(n_items - c0, CH);
     lds_barrier();  // the previous chunk's decisions are written out
-    int f_i = item_i(c0), f_hh = c0 % p.group;
-    int cur_i = f_i, cur_hh = f_hh;
-    for (int x = 0; x < PF && x < nc; ++x) {
-      fetch(kvh * p.group + f_hh, f_i, ring + x * SQ);
-      advance(f_i, f_hh);
+    int nf = 0;     // items of the chunk fetched so far
+    for (; nf < PF && nf < nc; ++nf) {
+      const int it = c0 + nf;
+      fetch(item_h(it), item_i(it), ring + nf * SQ);
     }
-    for (int k = 0; k < nc; ++k) {
-      const int i = cur_i;
-      advance(cur_i, cur_hh);
-      if (kStats || k + PF > nc)
-        vmcnt_wait<0>();
-      else
-        vmcnt_wait<(CPW + 1) * (PF - 1)>();
-      lds_barrier();  // Q of item k visible; flags of item k - 1 visible
-      if (k >= 1 && tid < NB) {
-        const int f = (k - 1) & 1;
-        dec_lds[tid][k - 1] = (flags[f][2 * tid] | flags[f][2 * tid + 1]) != 0 ? 1 : 0;
+    for (int k0 = 0; k0 < nc; k0 += 2) {
+      // items k0 and k0 + 1 landed (the later ones may stay in flight)
+      vmcnt_wait_le((nf - min(nc, k0 + 2)) * (CPW + 1));
+      lds_barrier();  // and visible; every wave is done with items k0 - 2, k0 - 1
+      for (int y = 0; y < 2 && nf < nc; ++y, ++nf) {
+        const int it = c0 + nf;
+        fetch(item_h(it), item_i(it), ring + (nf % RQ) * SQ);
       }
-      if (k + PF < nc) {
-        fetch(kvh * p.group + f_hh, f_i, ring + ((k + PF) % RQ) * SQ);
-        advance(f_i, f_hh);
-      }
+      const int k = k0 + par;
+      if (k >= nc) continue;
+      const int i = item_i(c0 + k);
       bool want = false;
-      if (legal(w >> 1, i)) {
+      if (legal(xb, i)) {
         const char* qt = ring + (k % RQ) * SQ;
-        const float* ri = (const float*)(qt + TB);
-        floatx4 s[4][2];
+        const float* wr = (const float*)(qt + TB);
+        // all B operands (Q^T: column 32 qs + l32) up front, then the products
+        bf16x8 bq[2][NDC];
 #pragma unroll
-        for (int qs = 0; qs < 4; ++qs) {
-          s[qs][0] = floatx4{0.f, 0.f, 0.f, 0.f};
-          s[qs][1] = floatx4{0.f, 0.f, 0.f, 0.f};
-        }
-        // all 16 A operands are read up front, then the 32 products
-        bf16x8 av[NDC][4];
+        for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+          for (int dc = 0; dc < NDC; ++dc) {
+            const int row = 32 * qs + l32;
+            const int ch = ((2 * dc + hh) ^ kswz32<D>(row)) & (KCH - 1);
+            bq[qs][dc] = *(const bf16x8*)(qt + row * D * 2 + ch * 16);
+          }
+        floatx16 s[2][2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) s[kt][qs][e] = 0.f;
 #pragma unroll
         for (int dc = 0; dc < NDC; ++dc)
 #pragma unroll
-          for (int qs = 0; qs < 4; ++qs) {
-            const int row = qperm(qs, l16);
-            const int ch = 4 * dc + g4;
-            av[dc][qs] = *(const bf16x8*)(qt + row * D * 2 + ((ch ^ dsw(row)) & (KCH - 1)) * 16);
-          }
-        __builtin_amdgcn_sched_barrier(0);
+          for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int dc = 0; dc < NDC; ++dc)
-#pragma unroll
-          for (int qs = 0; qs < 4; ++qs) {
-            s[qs][0] = mfma16x16x32(av[dc][qs], kreg[0][dc], s[qs][0]);
-            s[qs][1] = mfma16x16x32(av[dc][qs], kreg[1][dc], s[qs][1]);
-          }
+            for (int qs = 0; qs < 2; ++qs) s[kt][qs] = mfma32x32x16(kreg[kt][dc], bq[qs][dc], s[kt][qs]);
+        // register 4e' + r of subtile (kt, qs) holds key 32 kt + 8e' + 4hh + r
+        // of query column 32 qs + l32
         if ((p.causal && i == jw) || (64 * jw + 64 > p.nk)) {
 #pragma unroll
-          for (int qs = 0; qs < 4; ++qs)
+          for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int ns = 0; ns < 2; ++ns)
+            for (int qs = 0; qs < 2; ++qs)
 #pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const int qq = 64 * i + qperm(qs, 4 * g4 + r);
-                const bool ill = key[ns] >= p.nk || (p.causal && key[ns] > qq);
-                s[qs][ns][r] = ill ? -INFINITY : s[qs][ns][r];
+              for (int e = 0; e < 16; ++e) {
+                const int key = 64 * jw + 32 * kt + 8 * (e >> 2) + 4 * hh + (e & 3);
+                const int qq = 64 * i + 32 * qs + l32;
+                const bool ill = key >= p.nk || (p.causal && key > qq);
+                s[kt][qs][e] = ill ? -INFINITY : s[kt][qs][e];
               }
         }
         if constexpr (kTest) {
           // keep iff some legal entry has s >= W_q (masked entries are -inf;
-          // W_q = -inf only for tau = 0, where every legal tile is kept)
-          unsigned long long hit = 0;
+          // W_q = -inf only for tau = 0, where every legal tile is kept, and
+          // +inf for rows past the end)
+          bool hit = false;
 #pragma unroll
-          for (int qs = 0; qs < 4; ++qs) {
-            const float4 w4 = *(const float4*)(ri + 64 + 32 * (qs >> 1) + 8 * g4 + 4 * (qs & 1));
+          for (int qs = 0; qs < 2; ++qs) {
+            float mx = -INFINITY;
 #pragma unroll
-            for (int ns = 0; ns < 2; ++ns) {
-              hit |= __ballot(s[qs][ns][0] >= w4.x);
-              hit |= __ballot(s[qs][ns][1] >= w4.y);
-              hit |= __ballot(s[qs][ns][2] >= w4.z);
-              hit |= __ballot(s[qs][ns][3] >= w4.w);
-            }
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+              for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kt][qs][e]);
+            hit = hit || mx >= wr[32 * qs + l32];
           }
-          want = hit != 0;
+          want = wave_any(hit);
         } else {
           want = true;
         }
       }
-      if (lane == 0) flags[k & 1][w] = want ? 1 : 0;
-    }
-    lds_barrier();  // flags of the last item visible
-    if (tid < NB) {
-      const int f = (nc - 1) & 1;
-      dec_lds[tid][nc - 1] = (flags[f][2 * tid] | flags[f][2 * tid + 1]) != 0 ? 1 : 0;
+      if (lane == 0) dec_lds[xb][k] = want ? 1 : 0;
     }
     lds_barrier();  // the chunk's decisions visible
     // decisions of the legal tiles to the byte map (and the instrumentation)

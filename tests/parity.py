@@ -9,8 +9,11 @@ replaced by |a|*|b|).
     differ only where fp32 (kernel) and fp64 (model) intermediates round to
     different bf16 neighbours, each such flip moving one operand by at most
     2^-7 of itself, plus fp32 accumulation error; hence
-    |X_gpu - X_bf16| <= 2^-7 (M + |X_bf16| + M_D) + 1e-4, where M_D (backward
-    dQ, dK only) covers flips of the stored O inside D = rowsum(O o dO): each
+    |X_gpu - X_bf16| <= 2^-7 (M + |X_bf16| + M_D) + 1e-4. The backward is
+    held to V1 and V2 on the oracle's own forward outputs (bf16 O, fp32 LSE
+    fed to the GPU backward), so both sides form D = rowsum(O o dO) from the
+    same stored O and M_D = 0 there. M_D matters end to end, where the GPU
+    backward reads the GPU forward's O: a bf16 flip of a stored O element
     moves D_q by at most 2^-7 sum_d |O_qd dO_qd| and dS by P times that, so
     M_D is the dQ / dK sum with dS replaced by P * sum_d |O dO|;
   * V2: sum|X_gpu - X_bf16| / sum|X_bf16| <= 1e-3 (mean relative error);
