@@ -73,9 +73,13 @@ struct BwdParams {
   float scale;
   float c;         // scale * log2(e): raw score -> log2 units
   float log2_tau;  // log2(tau); -inf for tau = 0, +inf for tau = inf
-  int tr, tc, npair;
+  int tr, tc;
   long long dmap_per_head;   // bytes of the decision map per (batch, query head)
   int hpw, ipw, n_hg, n_ig;  // query-major grid (as the forward)
+  int* kcount;  // [B*Hkv*Tc] kept items per key block (scoring pass)
+  int* pairs;   // [B*Hkv][npair][2] key-block pairs of the dK/dV pass; -1 = none
+  int* segtab;  // [B*Hkv*Tc] segments of each key block's pair
+  int npair;    // pair slots per (batch, KV head)
   unsigned long long* counters;
   uint8_t* decisions;
 };
@@ -85,12 +89,6 @@ struct BwdParams {
 __device__ __forceinline__ long long dmap_index(const BwdParams& p, int bh, int i, int j) {
   const long long t = p.causal ? (long long)i * (i + 1) / 2 + j : (long long)i * p.tc + j;
   return (long long)bh * p.dmap_per_head + t;
-}
-
-// Segments of key block j's items (see kSegItems).
-__device__ __forceinline__ int kv_segments(const BwdParams& p, int j) {
-  const int n = p.group * (p.tr - (p.causal ? j : 0));
-  return min(p.seg_max, (n + kSegItems - 1) / kSegItems);
 }
 
 // MFMA row R of subtile x holds row 32(x/2) + 8(R/4) + 4(x%2) + R%4 of the
@@ -170,6 +168,7 @@ __global__ __launch_bounds__(512, 1) void bwd_score_kernel(BwdParams p) {
 
   __shared__ __attribute__((aligned(16))) char ring[RQ * SQ];
   __shared__ uint8_t dec_lds[NB][CH];
+  __shared__ int csum[8][NB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -228,6 +227,7 @@ __global__ __launch_bounds__(512, 1) void bwd_score_kernel(BwdParams p) {
     if (lane < 2) async_copy16_so(ri, (uint32_t)(16 * (2 * w + lane)), slot + TB + 32 * w);
   };
 
+  int kept = 0;  // kept items of key block jb0 + tid % NB seen by this thread
   for (int c0 = 0; c0 < n_items; c0 += CH) {
     const int nc = min(n_items - c0, CH);
     lds_barrier();  // the previous chunk's decisions are written out
@@ -320,6 +320,7 @@ __global__ __launch_bounds__(512, 1) void bwd_score_kernel(BwdParams p) {
       const int bh = b * p.heads_q + h;
       const uint8_t d = dec_lds[jx][kx];
       p.dmap[dmap_index(p, bh, i, jb0 + jx)] = d;
+      kept += d;
       if (kStats) {
         if (p.counters) {
           atomicAdd(&p.counters[0], 1ull);
@@ -332,6 +333,18 @@ __global__ __launch_bounds__(512, 1) void bwd_score_kernel(BwdParams p) {
       }
     }
     vmcnt_wait<0>();  // the stores are out before the next chunk's copies are counted
+  }
+  // kept items per key block (the write-out gives thread tid the blocks
+  // tid % NB): sum over the lanes and waves that share a block
+#pragma unroll
+  for (int off = NB; off < 64; off <<= 1) kept += __shfl_xor(kept, off);
+  if (lane < NB) csum[w][lane] = kept;
+  lds_barrier();
+  if (tid < NB && jb0 + tid < p.tc) {
+    int tot = 0;
+#pragma unroll
+    for (int y = 0; y < 8; ++y) tot += csum[y][tid];
+    p.kcount[(size_t)bk * p.tc + jb0 + tid] = tot;
   }
 }
 
@@ -346,26 +359,83 @@ __global__ __launch_bounds__(256) void bwd_dense_map_kernel(uint8_t* dmap, long 
   }
 }
 
+// --------------------------------------------------------------- pair ----
+// Key blocks are processed in pairs that share every Q and dO tile they
+// read. The pairs come from the kept-item counts of the scoring pass: blocks
+// that at least a quarter of their items keep (an attention sink, a
+// retrieval hub) keep nearly the same items, every query block after them,
+// so they are paired with each other in index order; the rest are paired in
+// index order among themselves. Heavy pairs come first in the table, so the
+// longest work is issued first. One workgroup per (batch, KV head).
+__global__ __launch_bounds__(256) void bwd_pair_kernel(BwdParams p) {
+  __shared__ int wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int bk = blockIdx.x;
+  const int* cnt = p.kcount + (size_t)bk * p.tc;
+  int* pairs = p.pairs + (size_t)bk * p.npair * 2;
+  auto heavy = [&](int j) {
+    const long long n = (long long)p.group * (p.tr - (p.causal ? j : 0));
+    return 4ll * cnt[j] >= n;
+  };
+  for (int x = tid; x < 2 * p.npair; x += 256) pairs[x] = -1;
+  // number of heavy blocks
+  int nh = 0;
+  for (int j0 = 0; j0 < p.tc; j0 += 256) {
+    const int j = j0 + tid;
+    const unsigned long long bal = __ballot(j < p.tc && heavy(j));
+    if (lane == 0) wsum[w] = __popcll(bal);
+    __syncthreads();
+    nh += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+  }
+  const int ph = (nh + 1) / 2;  // heavy pairs
+  int hrun = 0;                 // heavy blocks before this chunk
+  for (int j0 = 0; j0 < p.tc; j0 += 256) {
+    const int j = j0 + tid;
+    const bool hv = j < p.tc && heavy(j);
+    const unsigned long long bal = __ballot(hv);
+    if (lane == 0) wsum[w] = __popcll(bal);
+    __syncthreads();
+    int hidx = hrun + __popcll(bal & ((1ull << lane) - 1ull));
+    for (int y = 0; y < w; ++y) hidx += wsum[y];
+    if (j < p.tc) {
+      if (hv) {
+        pairs[hidx] = j;  // pair hidx / 2, slot hidx % 2
+      } else {
+        const int lidx = j - hidx;  // light blocks before j
+        pairs[2 * ph + lidx] = j;
+      }
+    }
+    hrun += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+  }
+}
+
 // ----------------------------------------------------------------- kv ----
-// dK, dV over the kept tiles. A workgroup of 4 wave64s owns one key block
-// (16 keys per wave; K and V as B operands, dK and dV accumulated in
-// registers); two workgroups share a CU. Per chunk of (query block, query
-// head) items it reads the block's decisions from the decision map, lists
-// the kept items, and runs their post-score work with Q, dO and the row
-// terms copied asynchronously into an LDS ring one entry ahead: S is
-// recomputed, P = exp2(s c - z2), dP = dO V^T, dS = P (dP - D),
-// dV += P^T dO, dK += dS^T Q (the transposed operands come from the
-// transposing LDS read).
+// dK, dV over the kept tiles. A workgroup of 4 wave64s (one per SIMD) owns
+// a pair of key blocks (or one): wave w holds keys 32 (w % 2) .. +31 of the
+// pair's block w / 2, with K and V as the B operands of S = Q K^T and
+// dP = dO V^T (32x32x16 bf16 MFMA) and dK^T, dV^T accumulated in registers.
+// Per chunk of (query block, query head) items it reads both blocks'
+// decisions from the decision map and lists the items either block keeps;
+// Q, dO and the row terms of a listed item are copied once, asynchronously,
+// into an LDS ring three entries ahead, and the waves of each block that
+// keeps it run the post-score work for 32 queries at a time: S is
+// recomputed, P = exp2(s c - z2), dS = P (dP - D); the S layout (a lane
+// holds one key and 16 queries) is already the B operand of
+// dV^T += dO^T P and dK^T += Q^T dS, whose A operands come from transposing
+// reads of the same Q and dO tiles.
 template <int D, bool kTest, bool kStats>
-__global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   constexpr int NT = 256;                // 4 wave64s
-  constexpr int NDC = D / 32;            // reduction chunks over d
-  constexpr int NDS = D / 16;            // 16-column subtiles of d
+  constexpr int NDC = D / 16;            // 16-wide reduction chunks over d
+  constexpr int NDT = D / 32;            // 32-row subtiles of dK^T, dV^T over d
   constexpr int KCH = D / 8;             // 16-byte chunks per row
   constexpr int TB = 64 * D * 2;         // bytes of a 64-row tile
-  constexpr int RB = kRowInfo * 4;       // bytes of a block's row terms
+  constexpr int RB = 2 * 64 * 4;         // z2 and D of the 64 rows
   constexpr int CPW = TB / 16 / NT;      // 16-byte copies per lane per tile
-  constexpr int RP = 2;                  // ring: the entry in use + the next
+  constexpr int OPS = 2 * CPW + 1;       // copies per wave per list entry
+  constexpr int RP = 4;                  // ring: the entry in use + 3 ahead
   constexpr int SP = 2 * TB + RB;        // ring slot: Q, dO, row terms
   constexpr int CH = 2048;               // items per chunk
 
@@ -375,58 +445,75 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int l16 = lane & 15, g4 = lane >> 4;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int sb = w >> 1, kh = w & 1;  // block of the pair, 32-key half
 
-  // ---- work item: segment seg of key block j of (b, kvh), longest blocks
-  //      first. (The dense path keeps one segment per block: its cost per
-  //      block is fixed, and whole blocks read the query blocks in the same
-  //      order, which the L2 shares between concurrent workgroups.) ----
+  // ---- work item: segment seg of pair pr of (b, kvh) ----
   const int per = p.batch * p.heads_kv;
   const int seg = (int)(blockIdx.x % p.seg_max);
-  const int j = (int)(blockIdx.x / p.seg_max / per);
+  const int pr = (int)(blockIdx.x / p.seg_max / per);
   const int bk = (int)(blockIdx.x / p.seg_max % per);
   const int b = bk / p.heads_kv, kvh = bk % p.heads_kv;
-  const int nseg = kv_segments(p, j);
-  if (seg >= nseg) return;  // (whole workgroup, before any barrier)
+  int jA, jB;
+  if (p.pairs) {
+    jA = p.pairs[((size_t)bk * p.npair + pr) * 2];
+    jB = p.pairs[((size_t)bk * p.npair + pr) * 2 + 1];
+  } else {  // blocks 2 pr and 2 pr + 1
+    jA = 2 * pr;
+    jB = 2 * pr + 1 < p.tc ? 2 * pr + 1 : -1;
+  }
+  if (jA < 0 || jA >= p.tc) return;  // no such pair (whole workgroup, before any barrier)
+  const int jlo = jB >= 0 ? min(jA, jB) : jA;
+  const int i_lo = p.causal ? jlo : 0;
+  const int n_all = p.group * (p.tr - i_lo);
+  const int nseg = min(p.seg_max, (n_all + kSegItems - 1) / kSegItems);
+  if (seg >= nseg) return;
+  if (seg == 0 && tid < 2 && p.segtab) {
+    const int jx = tid ? jB : jA;
+    if (jx >= 0) p.segtab[(size_t)bk * p.tc + jx] = nseg;
+  }
+  const int j = sb ? jB : jA;  // this wave's key block (-1: none)
   const __bf16* kbase = p.k + (size_t)bk * p.nk * D;
   const __bf16* vbase = p.v + (size_t)bk * p.nk * D;
 
-  // K and V of this wave's 16 keys as B operands
-  const int key = 64 * j + 16 * w + l16;
-  bf16x8 kreg[NDC], vreg[NDC];
+  // K and V of this lane's key (column l32 of the B operands), chunk
+  // 8 hh .. 8 hh + 7 of each 16-wide d chunk
+  const int key = 64 * j + 32 * kh + l32;
+  bf16x8 kb[NDC], vb[NDC];
   {
-    const bool ok = key < p.nk;
+    const bool ok = j >= 0 && key < p.nk;
 #pragma unroll
     for (int dc = 0; dc < NDC; ++dc) {
-      kreg[dc] = ok ? *(const bf16x8*)(kbase + (size_t)key * D + 32 * dc + 8 * g4) : bf16x8{};
-      vreg[dc] = ok ? *(const bf16x8*)(vbase + (size_t)key * D + 32 * dc + 8 * g4) : bf16x8{};
+      kb[dc] = ok ? *(const bf16x8*)(kbase + (size_t)key * D + 16 * dc + 8 * hh) : bf16x8{};
+      vb[dc] = ok ? *(const bf16x8*)(vbase + (size_t)key * D + 16 * dc + 8 * hh) : bf16x8{};
     }
   }
-  floatx4 dk_acc[NDS], dv_acc[NDS];
+  floatx16 dkt[NDT], dvt[NDT];
 #pragma unroll
-  for (int ds = 0; ds < NDS; ++ds) {
-    dk_acc[ds] = floatx4{0.f, 0.f, 0.f, 0.f};
-    dv_acc[ds] = floatx4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      dkt[dt][e] = 0.f;
+      dvt[dt][e] = 0.f;
+    }
 
   // items: query blocks from the last one down to the first with a legal
-  // entry for key block j, query heads of the group innermost
-  const int i_lo = p.causal ? j : 0;
-  const int n_all = p.group * (p.tr - i_lo);
+  // entry for either block, query heads of the group innermost
   const int seg_len = (n_all + nseg - 1) / nseg;
-  const int it0 = seg * seg_len;                       // this segment's items:
+  const int it0 = seg * seg_len;                        // this segment's items:
   const int n_items = min(n_all, it0 + seg_len) - it0;  // it0 .. it0 + n_items - 1
   auto item_i = [&](int it) { return p.tr - 1 - (it0 + it) / p.group; };
   auto item_h = [&](int it) { return kvh * p.group + (it0 + it) % p.group; };
+  auto legal = [&](int jx, int i) { return jx >= 0 && (!p.causal || i >= jx); };
 
   // ---- asynchronous tile copies: each wave moves a quarter of a tile and
-  //      of the row terms, so every wave issues CPW + 1 copies per tile ----
+  //      eight of the 32 row-term chunks ----
   uint32_t toff[CPW];  // byte offset within a full tile, per copy
 #pragma unroll
   for (int x = 0; x < CPW; ++x) {
     const int s = (4 * x + w) * 64 + lane;  // 16-byte chunk this lane fetches
     const int row = s / KCH, pc = s % KCH;
-    toff[x] = (uint32_t)(row * D * 2 + ((pc ^ dsw(row)) & (KCH - 1)) * 16);
+    toff[x] = (uint32_t)(row * D * 2 + ((pc ^ qswz32<D>(row)) & (KCH - 1)) * 16);
   }
   auto copy_tile = [&](const __bf16* rows0, int i, char* slot) {
     // rows0: row 0 of (b, h); block i lands swizzled in slot
@@ -440,33 +527,32 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdParams p) {
         const int s = (4 * x + w) * 64 + lane;
         const int row = s / KCH, pc = s % KCH;
         const int qq = min(64 * i + row, p.nq - 1);
-        async_copy16(rows0 + (size_t)qq * D + ((pc ^ dsw(row)) & (KCH - 1)) * 8,
+        async_copy16(rows0 + (size_t)qq * D + ((pc ^ qswz32<D>(row)) & (KCH - 1)) * 8,
                      slot + (4 * x + w) * 1024);
       }
     }
   };
+  // row terms: chunk c = 8w + lane (lanes 0..7) of [z2 x64][D x64]
+  const uint32_t roff = (uint32_t)(16 * (8 * w + (lane & 7)) + (w >= 2 ? 256 : 0));
   auto copy_rowinfo = [&](int h, int i, char* slot) {
     const float* src = p.rowinfo + ((size_t)(b * p.heads_q + h) * p.tr + i) * kRowInfo;
-    if (lane < 16) async_copy16_so(src, (uint32_t)(256 * w + 16 * lane), slot + 256 * w);
+    if (lane < 8) async_copy16_so(src, roff, slot + 128 * w);
   };
 
-  // A operand: rows qperm(qs, l16) of a row-major tile, reduction chunk dc
-  auto a_rows = [&](const char* t, int qs, int dc) {
-    const int row = qperm(qs, l16);
-    const int ch = 4 * dc + g4;
-    return *(const bf16x8*)(t + row * D * 2 + ((ch ^ dsw(row)) & (KCH - 1)) * 16);
-  };
-  // B operand: column 16 ds + l16 of a row-major tile over the 8 rows
-  // 32 kc + 8 g4 + 0..7, from two transposing reads
-  auto b_cols = [&](const char* t, int kc, int ds) {
+  // transposing-read coordinates (as the forward's V^T operand): a lane
+  // receives column 32 dt + l32 of rows 16 c + 4 hh + 0..3 (u = 0) and
+  // 16 c + 8 + 4 hh + 0..3 (u = 1)
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const int tr_row = 4 * (g16 >> 1) + (j16 >> 2);
+  const int tr_col = 16 * (g16 & 1) + 4 * (j16 & 3);
+  auto a_tr = [&](const __bf16* t, int r0, int dt) {
     short4v h2[2];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int row = 32 * kc + 8 * g4 + 4 * hh + (l16 >> 2);
-      const int col = 16 * ds + 4 * (l16 & 3);
-      h2[hh] = lds_read_tr4((const __bf16*)(t + row * D * 2 +
-                                            (((col >> 3) ^ dsw(row)) & (KCH - 1)) * 16 +
-                                            (col & 7) * 2));
+    for (int u = 0; u < 2; ++u) {
+      const int row = r0 + 8 * u + tr_row;
+      const int col = 32 * dt + tr_col;
+      const int ch = ((col >> 3) ^ qswz32<D>(row)) & (KCH - 1);
+      h2[u] = lds_read_tr4(t + row * D + ch * 8 + (col & 7));
     }
     return join_tr(h2[0], h2[1]);
   };
@@ -474,34 +560,36 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdParams p) {
   for (int c0 = 0; c0 < n_items; c0 += CH) {
     const int nc = min(n_items - c0, CH);
 
-    // ---- list of the chunk's items this key block keeps (decision map
-    //      written by the scoring pass) ----
+    // ---- list of the chunk's items either block keeps (decision map
+    //      written by the scoring pass): entry = item | keep mask << 28 ----
     lds_barrier();  // the previous chunk's list and ring are no longer read
     int n_list = 0;
     for (int x0 = 0; x0 < nc; x0 += NT) {
       const int x = x0 + tid;
-      bool kept = false;
+      int mask = 0;
       if (x < nc) {
         const int it = c0 + x;
         const int i = item_i(it), h = item_h(it);
-        kept = p.dmap[dmap_index(p, b * p.heads_q + h, i, j)] != 0;
-        if (kStats && kept && p.counters) atomicAdd(&p.counters[3], 1ull);
+        const int bh = b * p.heads_q + h;
+        if (legal(jA, i) && p.dmap[dmap_index(p, bh, i, jA)] != 0) mask |= 1;
+        if (legal(jB, i) && p.dmap[dmap_index(p, bh, i, jB)] != 0) mask |= 2;
+        if (kStats && p.counters && mask) atomicAdd(&p.counters[3], (unsigned long long)__popc(mask));
       }
-      const unsigned long long bal = __ballot(kept);
+      const unsigned long long bal = __ballot(mask != 0);
       const int before = __popcll(bal & ((1ull << lane) - 1ull));
       if (lane == 0) wcount[w] = __popcll(bal);
       lds_barrier();
       int off = n_list;
       for (int y = 0; y < w; ++y) off += wcount[y];
-      if (kept) list[off + before] = x;
+      if (mask) list[off + before] = x | (mask << 28);
       n_list += wcount[0] + wcount[1] + wcount[2] + wcount[3];
       lds_barrier();  // wcount reused; list entries visible
     }
     vmcnt_wait<0>();  // the map reads are done (the post phase counts copies only)
 
-    // ======== post-score work of the kept items, one entry ahead ========
+    // ======== post-score work of the listed items, three entries ahead ========
     auto issue_post = [&](int t) {
-      const int it = c0 + list[t];
+      const int it = c0 + (list[t] & 0xFFFFFFF);
       const int i = item_i(it), h = item_h(it);
       char* slot = ring + (t % RP) * SP;
       const size_t rows = (size_t)(b * p.heads_q + h) * p.nq * D;
@@ -509,121 +597,121 @@ __global__ __launch_bounds__(256, 2) void bwd_kv_kernel(BwdParams p) {
       copy_tile(p.dout + rows, i, slot + TB);
       copy_rowinfo(h, i, slot + 2 * TB);
     };
-    if (n_list > 0) issue_post(0);
+    int issued = 0;
+    for (; issued < RP - 1 && issued < n_list; ++issued) issue_post(issued);
     for (int t = 0; t < n_list; ++t) {
-      vmcnt_wait<0>();  // entry t landed (nothing later was issued yet)
-      lds_barrier();    // entry t visible; every wave is done with entry t - 1
-      if (t + 1 < n_list) issue_post(t + 1);
-      const int i = item_i(c0 + list[t]);
-      const char* qt = ring + (t % RP) * SP;
-      const char* dt = qt + TB;
-      const float* ri = (const float*)(qt + 2 * TB);
+      vmcnt_wait_le((issued - (t + 1)) * OPS);  // entry t landed
+      lds_barrier();  // entry t visible; every wave is done with entry t - 1
+      if (issued < n_list) {  // into the slot of entry t - 1
+        issue_post(issued);
+        ++issued;
+      }
+      const int e = list[t];
+      if (!((e >> (28 + sb)) & 1)) continue;
+      const int i = item_i(c0 + (e & 0xFFFFFFF));
+      const __bf16* qt = (const __bf16*)(ring + (t % RP) * SP);
+      const __bf16* dt_ = qt + 64 * D;
+      const float* ri = (const float*)(qt + 2 * 64 * D);
       const bool need_mask = (p.causal && i == j) || (64 * j + 64 > p.nk);
 #pragma unroll
-      for (int kc = 0; kc < 2; ++kc) {
-        // S (recomputed) and dP = dO V^T for query subtiles 2kc, 2kc + 1
-        bf16x8 aq[NDC][2], ao[NDC][2];
+      for (int qs = 0; qs < 2; ++qs) {
+        // S and dP for queries 32 qs .. 32 qs + 31: A = Q / dO rows
+        const int row = 32 * qs + l32;
+        floatx16 s, dp;
 #pragma unroll
-        for (int dc = 0; dc < NDC; ++dc)
-#pragma unroll
-          for (int x = 0; x < 2; ++x) {
-            aq[dc][x] = a_rows(qt, 2 * kc + x, dc);
-            ao[dc][x] = a_rows(dt, 2 * kc + x, dc);
-          }
-        __builtin_amdgcn_sched_barrier(0);
-        floatx4 s[2], dp[2];
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          s[x] = floatx4{0.f, 0.f, 0.f, 0.f};
-          dp[x] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int e2 = 0; e2 < 16; ++e2) {
+          s[e2] = 0.f;
+          dp[e2] = 0.f;
         }
 #pragma unroll
-        for (int dc = 0; dc < NDC; ++dc)
-#pragma unroll
-          for (int x = 0; x < 2; ++x) {
-            s[x] = mfma16x16x32(aq[dc][x], kreg[dc], s[x]);
-            dp[x] = mfma16x16x32(ao[dc][x], vreg[dc], dp[x]);
-          }
+        for (int dc = 0; dc < NDC; ++dc) {
+          const int ch = ((2 * dc + hh) ^ qswz32<D>(row)) & (KCH - 1);
+          const bf16x8 aq = *(const bf16x8*)(qt + row * D + ch * 8);
+          const bf16x8 ao = *(const bf16x8*)(dt_ + row * D + ch * 8);
+          s = mfma32x32x16(aq, kb[dc], s);
+          dp = mfma32x32x16(ao, vb[dc], dp);
+        }
+        // register 4e' + r holds query 32 qs + 8e' + 4hh + r of this lane's key
         if (need_mask) {
 #pragma unroll
-          for (int x = 0; x < 2; ++x)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int qq = 64 * i + qperm(2 * kc + x, 4 * g4 + r);
-              const bool ill = key >= p.nk || (p.causal && key > qq);
-              s[x][r] = ill ? -INFINITY : s[x][r];
-            }
+          for (int e2 = 0; e2 < 16; ++e2) {
+            const int qq = 64 * i + 32 * qs + 8 * (e2 >> 2) + 4 * hh + (e2 & 3);
+            const bool ill = key >= p.nk || (p.causal && key > qq);
+            s[e2] = ill ? -INFINITY : s[e2];
+          }
         }
-        // P = exp2(s c - z2), dS = P (dP - D), packed as A operands [key][query]
-        bf16x8 pa, da;
+        // P = exp2(s c - z2), dS = P (dP - D); chunk c2 of 16 queries is the
+        // B operand over queries 32 qs + 16 c2 + {4hh + 0..3, 8 + 4hh + 0..3}
+        bf16x8 pb[2], db[2];
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          const int ql = 32 * kc + 8 * g4 + 4 * x;
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int ql = 32 * qs + 8 * e4 + 4 * hh;
           const float4 z4 = *(const float4*)(ri + ql);
-          const float4 d4 = *(const float4*)(ri + 128 + ql);
+          const float4 d4 = *(const float4*)(ri + 64 + ql);
           const float zz[4] = {z4.x, z4.y, z4.z, z4.w};
           const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float pv = fast_exp2(s[x][r] * p.c - zz[r]);
-            pa[4 * x + r] = to_bf16(pv);
-            da[4 * x + r] = to_bf16(pv * (dp[x][r] - dd[r]));
+            const int e2 = 4 * e4 + r;
+            const float pv = fast_exp2(s[e2] * p.c - zz[r]);
+            pb[e4 >> 1][4 * (e4 & 1) + r] = to_bf16(pv);
+            db[e4 >> 1][4 * (e4 & 1) + r] = to_bf16(pv * (dp[e2] - dd[r]));
           }
         }
-        // dV += P^T dO, dK += dS^T Q over these 32 queries
+        // dV^T += dO^T P, dK^T += Q^T dS over these 32 queries
 #pragma unroll
-        for (int dh = 0; dh < 2; ++dh) {
-          bf16x8 bo[NDS / 2], bq[NDS / 2];
+        for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
-          for (int y = 0; y < NDS / 2; ++y) {
-            bo[y] = b_cols(dt, kc, dh * (NDS / 2) + y);
-            bq[y] = b_cols(qt, kc, dh * (NDS / 2) + y);
+          for (int d2 = 0; d2 < NDT; ++d2) {
+            dvt[d2] = mfma32x32x16(a_tr(dt_, 32 * qs + 16 * c2, d2), pb[c2], dvt[d2]);
+            dkt[d2] = mfma32x32x16(a_tr(qt, 32 * qs + 16 * c2, d2), db[c2], dkt[d2]);
           }
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int y = 0; y < NDS / 2; ++y) {
-            const int ds = dh * (NDS / 2) + y;
-            dv_acc[ds] = mfma16x16x32(pa, bo[y], dv_acc[ds]);
-            dk_acc[ds] = mfma16x16x32(da, bq[y], dk_acc[ds]);
-          }
-        }
       }
     }
   }
 
-  // ---- output rows = keys 4 g4 + r of this wave's 16: dK = scale * sum and
-  //      dV directly when the block has one segment, else fp32 partials ----
+  // ---- output: lane holds key 32 kh + l32 of block j, register 4e' + r of
+  //      subtile dt = column 32 dt + 8e' + 4hh + r: dK = scale * sum and dV
+  //      directly when the pair has one segment, else fp32 partials ----
+  if (j < 0) return;
   if (nseg == 1) {
+    if (key >= p.nk) return;
+    __bf16* dkr = p.dk + ((size_t)bk * p.nk + key) * D;
+    __bf16* dvr = p.dv + ((size_t)bk * p.nk + key) * D;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int kk = 64 * j + 16 * w + 4 * g4 + r;
-      if (kk >= p.nk) continue;
-      __bf16* dkr = p.dk + ((size_t)bk * p.nk + kk) * D;
-      __bf16* dvr = p.dv + ((size_t)bk * p.nk + kk) * D;
+    for (int d2 = 0; d2 < NDT; ++d2)
 #pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
-        dkr[16 * ds + l16] = to_bf16(dk_acc[ds][r] * p.scale);
-        dvr[16 * ds + l16] = to_bf16(dv_acc[ds][r]);
+      for (int e4 = 0; e4 < 4; ++e4) {
+        bf16x4 tk, tv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          tk[r] = to_bf16(dkt[d2][4 * e4 + r] * p.scale);
+          tv[r] = to_bf16(dvt[d2][4 * e4 + r]);
+        }
+        *(bf16x4*)(dkr + 32 * d2 + 8 * e4 + 4 * hh) = tk;
+        *(bf16x4*)(dvr + 32 * d2 + 8 * e4 + 4 * hh) = tv;
       }
-    }
   } else {
-    float* pk = p.part + (((size_t)bk * p.tc + j) * kSegMax + seg) * 2 * 64 * D;
+    const int row = 32 * kh + l32;
+    float* pk = p.part + (((size_t)bk * p.tc + j) * kSegMax + seg) * 2 * 64 * D + row * D;
     float* pv = pk + 64 * D;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 16 * w + 4 * g4 + r;
+    for (int d2 = 0; d2 < NDT; ++d2)
 #pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
-        pk[row * D + 16 * ds + l16] = dk_acc[ds][r];
-        pv[row * D + 16 * ds + l16] = dv_acc[ds][r];
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int col = 32 * d2 + 8 * e4 + 4 * hh;
+        *(float4*)(pk + col) = make_float4(dkt[d2][4 * e4], dkt[d2][4 * e4 + 1],
+                                           dkt[d2][4 * e4 + 2], dkt[d2][4 * e4 + 3]);
+        *(float4*)(pv + col) = make_float4(dvt[d2][4 * e4], dvt[d2][4 * e4 + 1],
+                                           dvt[d2][4 * e4 + 2], dvt[d2][4 * e4 + 3]);
       }
-    }
   }
 }
 
 // ----------------------------------------------------------- finalize ----
 // dK = scale * sum of the segments' partial sums, dV = their sum (segments
-// added in index order), for the key blocks split into several segments.
+// added in index order), for the key blocks whose pair was split into
+// several segments (the count is recorded per block by the dK/dV pass).
 template <int D>
 __global__ __launch_bounds__(256) void bwd_kv_finalize_kernel(BwdParams p) {
   const long long t = (long long)blockIdx.x * 256 + threadIdx.x;  // 8 values each
@@ -635,9 +723,9 @@ __global__ __launch_bounds__(256) void bwd_kv_finalize_kernel(BwdParams p) {
   const long long bj = e / D / 64;  // bk * Tc + j
   const int j = (int)(bj % p.tc);
   const long long bk = bj / p.tc;
-  const int nseg = kv_segments(p, j);
+  const int nseg = p.segtab[bj];
   const int kk = 64 * j + row;
-  if (nseg == 1 || kk >= p.nk) return;
+  if (nseg <= 1 || kk >= p.nk) return;
   float ak[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float av[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int sg = 0; sg < nseg; ++sg) {
@@ -905,8 +993,17 @@ hipError_t launch_all(const BwdParams& p, hipStream_t stream) {
   if (e != hipSuccess) return e;
   BwdParams q = p;
   q.seg_max = kTest ? kSegMax : 1;
+  if (kTest) {
+    hipLaunchKernelGGL(bwd_pair_kernel, dim3((unsigned)per), dim3(256), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else {
+    q.pairs = nullptr;  // dense: blocks 2 pr and 2 pr + 1 keep the same items
+    q.segtab = nullptr;
+  }
   hipLaunchKernelGGL((bwd_kv_kernel<D, kTest, kStats>),
-                     dim3((unsigned)((long long)p.tc * per * q.seg_max)), dim3(256), 0, stream, q);
+                     dim3((unsigned)((long long)p.npair * per * q.seg_max)), dim3(256), 0, stream,
+                     q);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (kTest) {
@@ -938,7 +1035,9 @@ size_t bwd_workspace_bytes(int batch, int heads_q, int heads_kv, int nq, int nk,
   const size_t per_head = causal ? tr * (tr + 1) / 2 : tr * tc;
   const size_t dmap = (size_t)batch * heads_q * per_head;
   const size_t part = (size_t)batch * heads_kv * tc * kSegMax * 2 * 64 * head_dim * sizeof(float);
-  return ((rowinfo + 255) & ~(size_t)255) + ((dmap + 255) & ~(size_t)255) + part;
+  const size_t npair = tc / 2 + 1;
+  const size_t tabs = (size_t)batch * heads_kv * (2 * tc + 2 * npair) * sizeof(int);
+  return ((rowinfo + 255) & ~(size_t)255) + ((dmap + 255) & ~(size_t)255) + part + tabs;
 }
 
 hipError_t launch_bwd(const BwdArgs& a, bool test, hipStream_t stream) {
@@ -964,13 +1063,17 @@ hipError_t launch_bwd(const BwdArgs& a, bool test, hipStream_t stream) {
   p.log2_tau = a.tau == 0.f ? -INFINITY : log2f(a.tau);
   p.tr = (a.nq + 63) / 64;
   p.tc = (a.nk + 63) / 64;
-  p.npair = (p.tc + 1) / 2;
   p.dmap_per_head = p.causal ? (long long)p.tr * (p.tr + 1) / 2 : (long long)p.tr * p.tc;
   const size_t rowinfo = (size_t)a.batch * a.heads_q * (size_t)p.tr * kRowInfo * sizeof(float);
   p.rowinfo = (float*)a.workspace;
   p.dmap = (uint8_t*)a.workspace + ((rowinfo + 255) & ~(size_t)255);
   const size_t dmap_bytes = (size_t)a.batch * a.heads_q * (size_t)p.dmap_per_head;
   p.part = (float*)(p.dmap + ((dmap_bytes + 255) & ~(size_t)255));
+  p.npair = p.tc / 2 + 1;
+  const size_t nkb = (size_t)a.batch * a.heads_kv * p.tc;
+  p.kcount = (int*)(p.part + nkb * kSegMax * 2 * 64 * a.head_dim);
+  p.segtab = p.kcount + nkb;
+  p.pairs = p.segtab + nkb;
   if (p.group % 4 == 0) {
     p.hpw = 4;
     p.ipw = 1;

@@ -289,6 +289,21 @@ __device__ __forceinline__ int vswz32(int row) {
   else return 2 * (row & 3);
 }
 
+// Tiles read both ways with the 32x32 shapes (the Q and dO tiles of the
+// dK/dV pass): row-major operand reads of 32 consecutive rows (one chunk
+// each) and the transposing reads of the V-type pattern above. Chunk bits
+// 2-3 and 1-2 follow row bits 0-1 one to one (distinct bank groups for the
+// transposing reads with 64 and 32 banks), and the whole XOR is one to one on
+// row bits 0-3 (distinct groups for 16 consecutive rows of the row-major
+// reads).
+template <int D>
+__device__ __forceinline__ int qswz32(int row) {
+  if constexpr (D == 128)
+    return (6 * (row & 1)) ^ (10 * ((row >> 1) & 1)) ^ ((row >> 2) & 1) ^ (8 * ((row >> 3) & 1));
+  else
+    return (2 * (row & 1)) ^ (4 * ((row >> 1) & 1)) ^ ((row >> 2) & 1) ^ (2 * ((row >> 3) & 1));
+}
+
 __device__ __forceinline__ int dsw(int row) {
   return (((row >> 3) ^ (row >> 4)) & 1) | ((row & 3) << 1) | (((row >> 3) & 1) << 3);
 }

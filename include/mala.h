@@ -117,19 +117,20 @@ int fullattn_fwd(const mala_shape* shape, const mala_config* cfg, const void* q,
  * D = rowsum(O o dO); 1 KiB per block), one decision byte per legal tile
  * (the lower triangle when causal), and fp32 partial dK/dV sums for up to 8
  * segments per 64-key block (8 x 2 x 64 x head_dim x 4 bytes per key block
- * and KV head: 512 KiB at head_dim 128). Returns 0 for an invalid shape or
- * config. */
+ * and KV head: 512 KiB at head_dim 128), and three int32 tables per (batch,
+ * KV head): kept items and segments per key block, and the Tc/2 + 1 key-block
+ * pairs the dK/dV pass runs (Tc = key blocks). Returns 0 for an invalid
+ * shape or config. */
 size_t mala_bwd_workspace_bytes(const mala_shape* shape, const mala_config* cfg);
 
 /* MALA backward (Algorithm 2; Eq. 4; the backward part of Appendix A.1).
- * A key-major pass visits, per (batch, KV head, pair of key blocks), every
- * query block with a legal entry for every query head of the group; Q.K is
- * recomputed and a tile is skipped when every legal entry has
- * s - z_q < log(tau / L_q), with z = the forward's LSE; otherwise
+ * A key-major scoring pass recomputes Q.K for every legal tile and skips a
+ * tile when every legal entry has s - z_q < log(tau / L_q), with z = the
+ * forward's LSE; the decisions are stored in the workspace. A key-major
+ * pass over pairs of key blocks then runs, for the kept tiles only,
  * P = exp(s - z), dP = dO V^T, dS = P o (dP - rowsum(O o dO)) and the dV and
- * dK products run. The decisions are stored in the workspace and a
- * query-major pass forms dQ over the kept tiles only (deterministic: no
- * atomics). o and lse are the forward's outputs. dQ, dK, dV are
+ * dK products, and a query-major pass forms dQ over the kept tiles
+ * (deterministic: no atomics). o and lse are the forward's outputs. dQ, dK, dV are
  * overwritten (rows without a kept tile get zeros). workspace must hold
  * mala_bwd_workspace_bytes(); its contents on entry are irrelevant. */
 int mala_bwd(const mala_shape* shape, const mala_config* cfg, const void* q, const void* k,
