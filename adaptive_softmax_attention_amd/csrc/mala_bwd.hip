@@ -5,38 +5,32 @@
 //
 // The offline test of Eq. 4 compares every legal score with the forward's
 // final log-normaliser, so a tile's decision does not depend on the order in
-// which tiles are visited and can be shared between passes. Three kernels on
-// the caller's stream:
+// which tiles are visited and can be shared between passes. Kernels on the
+// caller's stream:
 //   1. bwd_pre: per query row, D = rowsum(O o dO) in fp32 from the stored
 //      O, z2 = LSE * log2(e), and the test folded into one raw-score
 //      threshold W = (z2 + log2(tau / L_q)) / (scale * log2(e)): a legal
 //      entry keeps its tile iff s >= W. Written per 64-row block as
 //      [z2 x64][W x64][D x64][unused x64] (padded rows: z2 = W = +inf, so
 //      they neither pass the test nor contribute, P = 0).
-//   2. bwd_kv: key-major. A workgroup of 4 wave64s (one per SIMD, so each
-//      wave may hold up to 512 registers) owns 128 keys: key blocks 2J and
-//      2J + 1 of one KV head, two waves per block. Each wave holds its 32
-//      keys of K as MFMA B operands (S = Q K^T) and their dK, dV
-//      accumulators; V of the 128 keys sits in LDS. It visits (query block, query head) items from
-//      the last query block down to the diagonal, so the workgroups running
-//      at the same time read the same Q tiles (L2 reuse within an XCD).
-//      Per item: S is recomputed (16x16x32 bf16 MFMA), the test is one
-//      compare per score, a ballot per block and an OR over the 4 waves at
-//      a barrier. The decision goes to a byte map in the workspace. Only a
-//      kept tile requests dO; its post-score work (P, dP, dS, dV += P^T dO,
-//      dK += dS^T Q) runs one item later, so dO arrives while the next item
-//      is scored. Q (with the row terms) and dO are copied asynchronously
-//      from global memory into LDS rings; waves 0-1 issue the Q copies and
-//      waves 2-3 the dO copies, so each wave's in-order memory counter
-//      tracks a single stream. The transposed operands (dO and Q with the
-//      query index as reduction index) come from the transposing LDS read
-//      of the same tiles.
-//   3. bwd_dq: query-major, shaped like the forward (a wave pair per 64-row
+//   2. bwd_score: key-major scoring of every legal tile (S^T = K Q^T on
+//      32x32x16 MFMA, max-then-compare test per query column); writes the
+//      decision byte map and the kept-item count of every key block.
+//   3. bwd_pair: pairs the key blocks for the dK/dV pass by kept-item count
+//      (blocks most items keep, such as an attention sink or a retrieval
+//      hub, keep nearly the same items and are paired with each other).
+//   4. bwd_kv: key-major dK/dV over the kept tiles, one pair of key blocks
+//      per workgroup: each listed Q/dO tile is copied once for both blocks;
+//      long pairs are split into segments whose fp32 partial sums
+//      5. bwd_kv_finalize adds in a fixed order (deterministic, no atomics).
+//   6. bwd_dq: query-major, shaped like the forward (a wave pair per 64-row
 //      block, 4 blocks per workgroup sharing K/V tiles). It reads the byte
 //      map, lists the key blocks that some block of the workgroup keeps,
 //      and for those recomputes S^T = K Q^T and dP^T = V dO^T, forms
 //      dS^T and accumulates dQ^T += K^T dS^T in registers: dQ is written
 //      once, in bf16, with no atomics and no fp32 accumulator in memory.
+// The dense path fills the decision map with ones instead of scoring and
+// pairs blocks 2p, 2p + 1 without segments.
 #include <type_traits>
 
 #include "mala_common.h"
@@ -46,7 +40,7 @@ namespace mala {
 namespace {
 
 constexpr int kRowInfo = 256;  // floats of row terms per 64-row block
-// The dK/dV pass splits a key block's (query block, query head) items into at
+// The dK/dV pass splits a pair's (query block, query head) items into at
 // most kSegMax segments of about kSegItems items, one workgroup each, so that
 // a key block that every row keeps (an attention sink) does not serialise the
 // pass; the segments' fp32 partial sums are added in a fixed order by the
