@@ -134,212 +134,228 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 }
 
 // -------------------------------------------------------------- score ----
-// Offline test of every legal tile (Eq. 4), key-major. A workgroup of 8
-// wave64s owns 4 key blocks (256 keys) of one KV head. Wave w holds all 64
-// keys of block w % 4 as the A operand of S^T = K Q^T (32x32x16 bf16 MFMA,
-// fp32 accumulation) and scores every other item: waves 0-3 the even items,
-// waves 4-7 the odd ones, so the two waves on a SIMD share a key block and
-// each decides its own tiles with no exchange. Q tiles and the per-row
-// thresholds W_q stream through an LDS ring filled by asynchronous copies
-// (PF items ahead) from the last query block down; every workgroup walks the
-// items in the same order, so concurrent workgroups find each Q tile in L2.
-// A lane holds one query column of 32 keys per subtile: its test is the
-// maximum of those scores against W_q, then one ballot. Decisions go to the
-// byte map read by the dK/dV and dQ passes.
+// Offline test of every legal tile (Eq. 4), key-major. A workgroup owns 4 key
+// blocks (256 keys) of one KV head and walks every (query block, query head)
+// item from the last query block down; every workgroup walks the items in the
+// same order, so concurrent workgroups find each Q tile in L2.
+//   * Eight compute waves (two per SIMD): wave w holds all 64 keys of block
+//     w % 4 as the A operand of S^T = K Q^T (32x32x16 bf16 MFMA, fp32
+//     accumulation) and scores every other item (waves 0-3 the even items,
+//     waves 4-7 the odd ones), deciding its own tiles with no exchange. A
+//     lane holds one query column of 32 keys per subtile: its test is the
+//     maximum of those scores against W_q, then one ballot.
+//   * One copy wave moves each item's Q tile and thresholds from global
+//     memory into an LDS ring with asynchronous copies and publishes the item
+//     in the slot's flag once its copies have landed; the compute waves count
+//     their completions per slot, and the copy wave refills a slot only after
+//     all four of an item's waves are done with it. There is no workgroup
+//     barrier in the loop, and the compute waves issue no copies.
+//   * The copy wave publishes everything it has issued before it waits, so
+//     no wait can be circular. Every wait also has a bound far beyond any
+//     legal schedule; a wait that reached it would raise a workgroup flag that
+//     ends every other wait, so that every wave exits whatever happens.
+// Decisions go straight to the byte map read by the dK/dV and dQ passes; the
+// kept-item count of every key block goes to the pairing pass.
 template <int D, bool kTest, bool kStats>
-__global__ __launch_bounds__(512, 1) void bwd_score_kernel(BwdParams p) {
-  constexpr int NT = 512;
+__global__ __launch_bounds__(576, 1) void bwd_score_kernel(BwdParams p) {
+  constexpr int NC = 8;                  // compute waves
   constexpr int NDC = D / 16;            // 16-wide reduction chunks over d
   constexpr int KCH = D / 8;             // 16-byte chunks per row
   constexpr int TB = 64 * D * 2;         // bytes of a 64-row tile
   constexpr int WB = 64 * 4;             // bytes of a block's thresholds
   constexpr int SQ = TB + WB;            // ring slot
-  constexpr int CPW = TB / 16 / NT;      // tile copies per lane per item
-  constexpr int PF = 6;                  // items in flight
-  constexpr int RQ = PF + 2;             // + the two in use
+  constexpr int CPI = TB / 16 / 64;      // tile copies of the copy wave per item
+  constexpr int OPS = CPI + 1;           // + the thresholds
+  constexpr int LAG = 3;                 // items the copy wave keeps in flight
+  static_assert(OPS * LAG < 64, "vmcnt range");
+  constexpr int RQ = 8;                  // ring slots (even: a slot keeps its parity)
   constexpr int NB = 4;                  // key blocks per workgroup
-  constexpr int CH = 1024;               // items per chunk (decisions held in LDS)
+  constexpr int kSpin = 1 << 22;         // bound on every wait (in sleeps)
 
   __shared__ __attribute__((aligned(16))) char ring[RQ * SQ];
-  __shared__ uint8_t dec_lds[NB][CH];
-  __shared__ int csum[8][NB];
+  __shared__ int full[RQ];  // 1 + the item whose data the slot holds
+  __shared__ int done[RQ];  // compute-wave completions of the slot's items
+  __shared__ int csum[NC];
+  __shared__ int stop;      // set by a wait that reached its bound
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, hh = lane >> 5;
-  const int xb = w & 3;   // key block of this wave within the group
-  const int par = w >> 2; // parity of the items this wave scores
 
   const int per = p.batch * p.heads_kv;
   const int G4 = (int)(blockIdx.x / per);  // key blocks 4 G4 .. 4 G4 + 3, longest first
   const int bk = (int)(blockIdx.x % per);
   const int b = bk / p.heads_kv, kvh = bk % p.heads_kv;
   const int jb0 = NB * G4;
-  const int jw = jb0 + xb;  // this wave's key block
-  const __bf16* kbase = p.k + (size_t)bk * p.nk * D;
-
-  // K of the 64 keys as A operands: subtile kt, lane row 32 kt + l32
-  bf16x8 kreg[2][NDC];
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-    const int key = 64 * jw + 32 * kt + l32;
-    const bool ok = jw < p.tc && key < p.nk;
-#pragma unroll
-    for (int dc = 0; dc < NDC; ++dc)
-      kreg[kt][dc] = ok ? *(const bf16x8*)(kbase + (size_t)key * D + 16 * dc + 8 * hh) : bf16x8{};
-  }
-  // retire the register loads here: the asynchronous copies below are not
-  // counted by the compiler's own waits
-  vmcnt_wait<0>();
-
-  // key block x (0..3) of this workgroup has a legal entry for query block i
-  auto legal = [&](int x, int i) {
-    const int j = jb0 + x;
-    return j < p.tc && (!p.causal || i >= j);
-  };
   const int i_lo = p.causal ? jb0 : 0;
   const int n_items = p.group * (p.tr - i_lo);
   auto item_i = [&](int it) { return p.tr - 1 - it / p.group; };
   auto item_h = [&](int it) { return kvh * p.group + it % p.group; };
 
-  // copies of item (h, i): CPW tile chunks per lane (row-major, chunks
-  // XOR-swizzled per row as the 32-row operand reads expect) and two of the
-  // 16 threshold chunks per wave
-  auto fetch = [&](int h, int i, char* slot) {
-    const __bf16* rows0 = p.q + (size_t)(b * p.heads_q + h) * p.nq * D;
-    const int last = p.nq - 1 - 64 * i;  // last row inside the queries
-#pragma unroll
-    for (int x = 0; x < CPW; ++x) {
-      const int s0 = x * NT + w * 64;
-      const int s = s0 + lane;
-      const int row = s / KCH, pc = s % KCH;
-      const uint32_t voff =
-          (uint32_t)((min(row, last) * D + ((pc ^ kswz32<D>(row)) & (KCH - 1)) * 8) * 2);
-      async_copy16_so(rows0 + (size_t)64 * i * D, voff, slot + s0 * 16);
+  if (tid < RQ) {
+    full[tid] = 0;
+    done[tid] = 0;
+  }
+  if (tid == 0) stop = 0;
+  lds_barrier();
+  // wait until ready() holds (false only if the bound was reached somewhere)
+  auto wait_for = [&](auto ready) {
+    for (int g = 0; !ready(); ++g) {
+      if (__hip_atomic_load(&stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) return;
+      if (g >= kSpin) {
+        __hip_atomic_store(&stop, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        return;
+      }
+      __builtin_amdgcn_s_sleep(1);
     }
-    const float* ri = p.rowinfo + ((size_t)(b * p.heads_q + h) * p.tr + i) * kRowInfo + 64;
-    if (lane < 2) async_copy16_so(ri, (uint32_t)(16 * (2 * w + lane)), slot + TB + 32 * w);
   };
 
-  int kept = 0;  // kept items of key block jb0 + tid % NB seen by this thread
-  for (int c0 = 0; c0 < n_items; c0 += CH) {
-    const int nc = min(n_items - c0, CH);
-    lds_barrier();  // the previous chunk's decisions are written out
-    int nf = 0;     // items of the chunk fetched so far
-    for (; nf < PF && nf < nc; ++nf) {
-      const int it = c0 + nf;
-      fetch(item_h(it), item_i(it), ring + nf * SQ);
-    }
-    for (int k0 = 0; k0 < nc; k0 += 2) {
-      // items k0 and k0 + 1 landed (the later ones may stay in flight)
-      vmcnt_wait_le((nf - min(nc, k0 + 2)) * (CPW + 1));
-      lds_barrier();  // and visible; every wave is done with items k0 - 2, k0 - 1
-      for (int y = 0; y < 2 && nf < nc; ++y, ++nf) {
-        const int it = c0 + nf;
-        fetch(item_h(it), item_i(it), ring + (nf % RQ) * SQ);
-      }
-      const int k = k0 + par;
-      if (k >= nc) continue;
-      const int i = item_i(c0 + k);
-      bool want = false;
-      if (legal(xb, i)) {
-        const char* qt = ring + (k % RQ) * SQ;
-        const float* wr = (const float*)(qt + TB);
-        // all B operands (Q^T: column 32 qs + l32) up front, then the products
-        bf16x8 bq[2][NDC];
+  if (w == NC) {
+    // ======== copy wave ========
+    // copies of item it: row-major tile, chunks XOR-swizzled per row as the
+    // 32-row operand reads expect (rows past the end re-read the last row),
+    // then the 64 thresholds
+    auto fetch = [&](int it, char* slot) {
+      const int h = item_h(it), i = item_i(it);
+      const __bf16* rows0 = p.q + ((size_t)(b * p.heads_q + h) * p.nq + (size_t)64 * i) * D;
+      const int last = p.nq - 1 - 64 * i;  // last row inside the queries
 #pragma unroll
-        for (int qs = 0; qs < 2; ++qs)
+      for (int x = 0; x < CPI; ++x) {
+        const int s = x * 64 + lane;
+        const int row = s / KCH, pc = s % KCH;
+        const uint32_t voff =
+            (uint32_t)((min(row, last) * D + ((pc ^ kswz32<D>(row)) & (KCH - 1)) * 8) * 2);
+        async_copy16_so(rows0, voff, slot + x * 1024);
+      }
+      const float* ri = p.rowinfo + ((size_t)(b * p.heads_q + h) * p.tr + i) * kRowInfo + 64;
+      if (lane < 16) async_copy16_so(ri, (uint32_t)(16 * lane), slot + TB);
+    };
+    auto publish = [&](int it) {
+      if (lane == 0)
+        __hip_atomic_store(&full[it % RQ], it + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+    int marked = 0;  // items published so far
+    for (int nf = 0; nf < n_items; ++nf) {
+      if (nf >= RQ) {
+        // the slot's previous item must be released by its four compute waves
+        const int need = NB * (nf / RQ);
+        if (__hip_atomic_load(&done[nf % RQ], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < need) {
+          vmcnt_wait<0>();  // publish everything issued before waiting
+          while (marked < nf) publish(marked++);
+          wait_for([&] {
+            return __hip_atomic_load(&done[nf % RQ], __ATOMIC_ACQUIRE,
+                                     __HIP_MEMORY_SCOPE_WORKGROUP) >= need;
+          });
+        }
+      }
+      fetch(nf, ring + (nf % RQ) * SQ);
+      if (nf + 1 - marked > LAG) {  // keep LAG items in flight, publish the older ones
+        vmcnt_wait<OPS * LAG>();
+        while (marked <= nf - LAG) publish(marked++);
+      }
+    }
+    vmcnt_wait<0>();
+    while (marked < n_items) publish(marked++);
+  } else {
+    // ======== compute waves ========
+    const int xb = w & 3;    // key block of this wave within the group
+    const int par = w >> 2;  // parity of the items this wave scores
+    const int jw = jb0 + xb;
+    const bool live = jw < p.tc;
+    const __bf16* kbase = p.k + (size_t)bk * p.nk * D;
+    // K of the 64 keys as A operands: subtile kt, lane row 32 kt + l32
+    bf16x8 kreg[2][NDC];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int key = 64 * jw + 32 * kt + l32;
+      const bool ok = live && key < p.nk;
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc)
+        kreg[kt][dc] = ok ? *(const bf16x8*)(kbase + (size_t)key * D + 16 * dc + 8 * hh) : bf16x8{};
+    }
+    int kept = 0;
+    for (int k = par; k < n_items; k += 2) {
+      const int slot = k % RQ;
+      wait_for([&] {
+        return __hip_atomic_load(&full[slot], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) ==
+               k + 1;
+      });
+      const int i = item_i(k);
+      if (live && (!p.causal || i >= jw)) {
+        const char* qt = ring + slot * SQ;
+        const float* wr = (const float*)(qt + TB);
+        const bool need_mask = (p.causal && i == jw) || (64 * jw + 64 > p.nk);
+        bool hit = false;
+#pragma unroll
+        for (int qs = 0; qs < 2; ++qs) {
+          // B operands (Q^T: column 32 qs + l32) up front, then the products
+          bf16x8 bq[NDC];
 #pragma unroll
           for (int dc = 0; dc < NDC; ++dc) {
             const int row = 32 * qs + l32;
             const int ch = ((2 * dc + hh) ^ kswz32<D>(row)) & (KCH - 1);
-            bq[qs][dc] = *(const bf16x8*)(qt + row * D * 2 + ch * 16);
+            bq[dc] = *(const bf16x8*)(qt + row * D * 2 + ch * 16);
           }
-        floatx16 s[2][2];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int qs = 0; qs < 2; ++qs)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) s[kt][qs][e] = 0.f;
-#pragma unroll
-        for (int dc = 0; dc < NDC; ++dc)
+          floatx16 s[2];
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int qs = 0; qs < 2; ++qs) s[kt][qs] = mfma32x32x16(kreg[kt][dc], bq[qs][dc], s[kt][qs]);
-        // register 4e' + r of subtile (kt, qs) holds key 32 kt + 8e' + 4hh + r
-        // of query column 32 qs + l32
-        if ((p.causal && i == jw) || (64 * jw + 64 > p.nk)) {
+            for (int e = 0; e < 16; ++e) s[kt][e] = 0.f;
 #pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
+          for (int dc = 0; dc < NDC; ++dc)
 #pragma unroll
-            for (int qs = 0; qs < 2; ++qs)
+            for (int kt = 0; kt < 2; ++kt) s[kt] = mfma32x32x16(kreg[kt][dc], bq[dc], s[kt]);
+          // register 4e' + r of subtile kt holds key 32 kt + 8e' + 4hh + r
+          // of query column 32 qs + l32
+          if (need_mask) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
               for (int e = 0; e < 16; ++e) {
                 const int key = 64 * jw + 32 * kt + 8 * (e >> 2) + 4 * hh + (e & 3);
                 const int qq = 64 * i + 32 * qs + l32;
                 const bool ill = key >= p.nk || (p.causal && key > qq);
-                s[kt][qs][e] = ill ? -INFINITY : s[kt][qs][e];
+                s[kt][e] = ill ? -INFINITY : s[kt][e];
               }
-        }
-        if constexpr (kTest) {
+          }
           // keep iff some legal entry has s >= W_q (masked entries are -inf;
           // W_q = -inf only for tau = 0, where every legal tile is kept, and
           // +inf for rows past the end)
-          bool hit = false;
+          float mx = -INFINITY;
 #pragma unroll
-          for (int qs = 0; qs < 2; ++qs) {
-            float mx = -INFINITY;
+          for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-              for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kt][qs][e]);
-            hit = hit || mx >= wr[32 * qs + l32];
-          }
-          want = wave_any(hit);
-        } else {
-          want = true;
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kt][e]);
+          hit = hit || mx >= wr[32 * qs + l32];
         }
-      }
-      if (lane == 0) dec_lds[xb][k] = want ? 1 : 0;
-    }
-    lds_barrier();  // the chunk's decisions visible
-    // decisions of the legal tiles to the byte map (and the instrumentation)
-    for (int x = tid; x < nc * NB; x += NT) {
-      const int kx = x / NB, jx = x % NB;
-      const int it = c0 + kx;
-      const int i = item_i(it), h = item_h(it);
-      if (!legal(jx, i)) continue;
-      const int bh = b * p.heads_q + h;
-      const uint8_t d = dec_lds[jx][kx];
-      p.dmap[dmap_index(p, bh, i, jb0 + jx)] = d;
-      kept += d;
-      if (kStats) {
-        if (p.counters) {
-          atomicAdd(&p.counters[0], 1ull);
-          if (d) {
-            atomicAdd(&p.counters[1], 1ull);
-            atomicAdd(&p.counters[2], (unsigned long long)min(64, p.nq - 64 * i) * 64ull);
+        const bool want = kTest ? wave_any(hit) : true;
+        kept += want ? 1 : 0;
+        if (lane == 0) {
+          const int bh = b * p.heads_q + item_h(k);
+          p.dmap[dmap_index(p, bh, i, jw)] = want ? 1 : 0;
+          if (kStats) {
+            if (p.counters) {
+              atomicAdd(&p.counters[0], 1ull);
+              if (want) {
+                atomicAdd(&p.counters[1], 1ull);
+                atomicAdd(&p.counters[2], (unsigned long long)min(64, p.nq - 64 * i) * 64ull);
+              }
+            }
+            if (p.decisions) p.decisions[((size_t)bh * p.tr + i) * p.tc + jw] = want ? 1 : 0;
           }
         }
-        if (p.decisions) p.decisions[((size_t)bh * p.tr + i) * p.tc + jb0 + jx] = d;
       }
+      // release the slot (this wave's reads of it have completed: the
+      // products consumed them, and LDS operations of a wave complete in order)
+      if (lane == 0)
+        __hip_atomic_fetch_add(&done[slot], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
-    vmcnt_wait<0>();  // the stores are out before the next chunk's copies are counted
+    if (lane == 0) csum[w] = kept;
   }
-  // kept items per key block (the write-out gives thread tid the blocks
-  // tid % NB): sum over the lanes and waves that share a block
-#pragma unroll
-  for (int off = NB; off < 64; off <<= 1) kept += __shfl_xor(kept, off);
-  if (lane < NB) csum[w][lane] = kept;
   lds_barrier();
-  if (tid < NB && jb0 + tid < p.tc) {
-    int tot = 0;
-#pragma unroll
-    for (int y = 0; y < 8; ++y) tot += csum[y][tid];
-    p.kcount[(size_t)bk * p.tc + jb0 + tid] = tot;
-  }
+  // kept items per key block (waves x and x + 4 score block x)
+  if (tid < NB && jb0 + tid < p.tc)
+    p.kcount[(size_t)bk * p.tc + jb0 + tid] = csum[tid] + csum[tid + 4];
 }
 
 // Dense path without instrumentation: every legal tile is kept, so the
@@ -977,7 +993,7 @@ hipError_t launch_all(const BwdParams& p, hipStream_t stream) {
   const long long per = (long long)p.batch * p.heads_kv;
   if (kTest || kStats) {
     hipLaunchKernelGGL((bwd_score_kernel<D, kTest, kStats>),
-                       dim3((unsigned)(((p.tc + 3) / 4) * per)), dim3(512), 0, stream, p);
+                       dim3((unsigned)(((p.tc + 3) / 4) * per)), dim3(576), 0, stream, p);
   } else {
     const long long n = (long long)p.batch * p.heads_q * p.dmap_per_head;
     hipLaunchKernelGGL(bwd_dense_map_kernel, dim3((unsigned)((n + 4095) / 4096)), dim3(256), 0,
