@@ -41,11 +41,12 @@ namespace {
 
 constexpr int kRowInfo = 256;  // floats of row terms per 64-row block
 // The dK/dV pass splits a pair's (query block, query head) items into at
-// most kSegMax segments of about kSegItems items, one workgroup each, so that
-// a key block that every row keeps (an attention sink) does not serialise the
-// pass; the segments' fp32 partial sums are added in a fixed order by the
-// finalize kernel (deterministic, no atomics).
-constexpr int kSegItems = 2048;
+// most kSegMax equal segments, one workgroup each, about one per kSegKept
+// items the pair keeps, so that a key block that every row keeps (an
+// attention sink) does not serialise the pass; the segments' fp32 partial
+// sums are added in a fixed order by the finalize kernel (deterministic, no
+// atomics).
+constexpr int kSegKept = 512;
 constexpr int kSegMax = 8;
 
 struct BwdParams {
@@ -61,7 +62,6 @@ struct BwdParams {
   float* rowinfo;  // [B*Hq*Tr][kRowInfo]
   uint8_t* dmap;   // backward decisions, see dmap_index()
   float* part;     // [B*Hkv*Tc][kSegMax][2][64][D] fp32 partial dK, dV
-  int seg_max;     // segments per key block at most: kSegMax (MALA) or 1 (dense)
   int batch, heads_q, heads_kv, nq, nk, group;
   int causal;
   float scale;
@@ -74,6 +74,9 @@ struct BwdParams {
   int* pairs;   // [B*Hkv][npair][2] key-block pairs of the dK/dV pass; -1 = none
   int* segtab;  // [B*Hkv*Tc] segments of each key block's pair
   int npair;    // pair slots per (batch, KV head)
+  int* work;    // [B*Hkv][wmax] dK/dV work items: pair | seg << 20 | nseg << 24
+  int* wcnt;    // [B*Hkv] work items per (batch, KV head)
+  int wmax;     // work item slots per (batch, KV head)
   unsigned long long* counters;
   uint8_t* decisions;
 };
@@ -376,9 +379,13 @@ __global__ __launch_bounds__(256) void bwd_dense_map_kernel(uint8_t* dmap, long 
 // retrieval hub) keep nearly the same items, every query block after them,
 // so they are paired with each other in index order; the rest are paired in
 // index order among themselves. Heavy pairs come first in the table, so the
-// longest work is issued first. One workgroup per (batch, KV head).
+// longest work is issued first. Each pair is then split into segments, about
+// one per kSegKept items the pair keeps (at most kSegMax), and the
+// (pair, segment) work items are listed in table order for the dK/dV pass.
+// One workgroup per (batch, KV head).
 __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdParams p) {
   __shared__ int wsum[4];
+  __shared__ int scan[256];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int bk = blockIdx.x;
   const int* cnt = p.kcount + (size_t)bk * p.tc;
@@ -419,6 +426,34 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdParams p) {
     hrun += wsum[0] + wsum[1] + wsum[2] + wsum[3];
     __syncthreads();
   }
+  // work items, in table order (the barrier above also made the table
+  // visible to the whole workgroup)
+  int* work = p.work + (size_t)bk * p.wmax;
+  int base = 0;
+  for (int x0 = 0; x0 < p.npair; x0 += 256) {
+    const int pr = x0 + tid;
+    int nseg = 0;
+    if (pr < p.npair) {
+      const int jA = pairs[2 * pr], jB = pairs[2 * pr + 1];
+      if (jA >= 0) {
+        const int kept = cnt[jA] + (jB >= 0 ? cnt[jB] : 0);
+        nseg = min(kSegMax, max(1, (kept + kSegKept - 1) / kSegKept));
+      }
+    }
+    scan[tid] = nseg;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {  // inclusive prefix sum
+      const int v = tid >= off ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    const int first = base + scan[tid] - nseg;
+    for (int sg = 0; sg < nseg; ++sg) work[first + sg] = pr | (sg << 20) | (nseg << 24);
+    base += scan[255];
+    __syncthreads();
+  }
+  if (tid == 0) p.wcnt[bk] = base;
 }
 
 // ----------------------------------------------------------------- kv ----
@@ -458,26 +493,38 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   const int l32 = lane & 31, hh = lane >> 5;
   const int sb = w >> 1, kh = w & 1;  // block of the pair, 32-key half
 
-  // ---- work item: segment seg of pair pr of (b, kvh) ----
+  // ---- work item b of the list the pairing pass wrote (MALA), or pair b
+  //      (dense), the first item of every (batch, KV head) first; the grid
+  //      bounds the list, and workgroups past its end exit at once. Items
+  //      are issued in list order (longest first) and consecutive items,
+  //      such as the segments of one pair, go to different XCDs ----
   const int per = p.batch * p.heads_kv;
-  const int seg = (int)(blockIdx.x % p.seg_max);
-  const int pr = (int)(blockIdx.x / p.seg_max / per);
-  const int bk = (int)(blockIdx.x / p.seg_max % per);
+  const int bk = (int)(blockIdx.x % per), idx = (int)(blockIdx.x / per);
+  int pr, seg, nseg;
+  if (p.pairs) {
+    if (idx >= p.wcnt[bk]) return;  // (whole workgroup, before any barrier)
+    const int wi = p.work[(size_t)bk * p.wmax + idx];
+    pr = wi & 0xFFFFF;
+    seg = (wi >> 20) & 15;
+    nseg = wi >> 24;
+  } else {  // dense: blocks 2 pr and 2 pr + 1, one segment
+    if (idx >= (p.tc + 1) / 2) return;
+    pr = idx;
+    seg = 0;
+    nseg = 1;
+  }
   const int b = bk / p.heads_kv, kvh = bk % p.heads_kv;
   int jA, jB;
   if (p.pairs) {
     jA = p.pairs[((size_t)bk * p.npair + pr) * 2];
     jB = p.pairs[((size_t)bk * p.npair + pr) * 2 + 1];
-  } else {  // blocks 2 pr and 2 pr + 1
+  } else {
     jA = 2 * pr;
     jB = 2 * pr + 1 < p.tc ? 2 * pr + 1 : -1;
   }
-  if (jA < 0 || jA >= p.tc) return;  // no such pair (whole workgroup, before any barrier)
   const int jlo = jB >= 0 ? min(jA, jB) : jA;
   const int i_lo = p.causal ? jlo : 0;
   const int n_all = p.group * (p.tr - i_lo);
-  const int nseg = min(p.seg_max, (n_all + kSegItems - 1) / kSegItems);
-  if (seg >= nseg) return;
   if (seg == 0 && tid < 2 && p.segtab) {
     const int jx = tid ? jB : jA;
     if (jx >= 0) p.segtab[(size_t)bk * p.tc + jx] = nseg;
@@ -1002,7 +1049,6 @@ hipError_t launch_all(const BwdParams& p, hipStream_t stream) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   BwdParams q = p;
-  q.seg_max = kTest ? kSegMax : 1;
   if (kTest) {
     hipLaunchKernelGGL(bwd_pair_kernel, dim3((unsigned)per), dim3(256), 0, stream, p);
     e = hipGetLastError();
@@ -1012,8 +1058,8 @@ hipError_t launch_all(const BwdParams& p, hipStream_t stream) {
     q.segtab = nullptr;
   }
   hipLaunchKernelGGL((bwd_kv_kernel<D, kTest, kStats>),
-                     dim3((unsigned)((long long)p.npair * per * q.seg_max)), dim3(256), 0, stream,
-                     q);
+                     dim3((unsigned)((long long)(kTest ? p.wmax : p.npair) * per)), dim3(256), 0,
+                     stream, q);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (kTest) {
@@ -1046,7 +1092,7 @@ size_t bwd_workspace_bytes(int batch, int heads_q, int heads_kv, int nq, int nk,
   const size_t dmap = (size_t)batch * heads_q * per_head;
   const size_t part = (size_t)batch * heads_kv * tc * kSegMax * 2 * 64 * head_dim * sizeof(float);
   const size_t npair = tc / 2 + 1;
-  const size_t tabs = (size_t)batch * heads_kv * (2 * tc + 2 * npair) * sizeof(int);
+  const size_t tabs = (size_t)batch * heads_kv * (2 * tc + 2 * npair + npair * kSegMax + 1) * sizeof(int);
   return ((rowinfo + 255) & ~(size_t)255) + ((dmap + 255) & ~(size_t)255) + part + tabs;
 }
 
@@ -1084,6 +1130,10 @@ hipError_t launch_bwd(const BwdArgs& a, bool test, hipStream_t stream) {
   p.kcount = (int*)(p.part + nkb * kSegMax * 2 * 64 * a.head_dim);
   p.segtab = p.kcount + nkb;
   p.pairs = p.segtab + nkb;
+  const size_t nbk = (size_t)a.batch * a.heads_kv;
+  p.wmax = p.npair * kSegMax;
+  p.work = p.pairs + nbk * p.npair * 2;
+  p.wcnt = p.work + nbk * p.wmax;
   if (p.group % 4 == 0) {
     p.hpw = 4;
     p.ipw = 1;

@@ -117,10 +117,10 @@ int fullattn_fwd(const mala_shape* shape, const mala_config* cfg, const void* q,
  * D = rowsum(O o dO); 1 KiB per block), one decision byte per legal tile
  * (the lower triangle when causal), and fp32 partial dK/dV sums for up to 8
  * segments per 64-key block (8 x 2 x 64 x head_dim x 4 bytes per key block
- * and KV head: 512 KiB at head_dim 128), and three int32 tables per (batch,
- * KV head): kept items and segments per key block, and the Tc/2 + 1 key-block
- * pairs the dK/dV pass runs (Tc = key blocks). Returns 0 for an invalid
- * shape or config. */
+ * and KV head: 512 KiB at head_dim 128), and int32 tables per (batch, KV
+ * head): kept items and segments per key block, the Tc/2 + 1 key-block pairs
+ * the dK/dV pass runs and up to 8 work items per pair, and the work count
+ * (Tc = key blocks). Returns 0 for an invalid shape or config. */
 size_t mala_bwd_workspace_bytes(const mala_shape* shape, const mala_config* cfg);
 
 /* MALA backward (Algorithm 2; Eq. 4; the backward part of Appendix A.1).

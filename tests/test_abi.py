@@ -109,14 +109,15 @@ def test_workspace_sizes():
     # byte per legal tile (lower triangle when causal, Tr x Tc otherwise),
     # plus fp32 partial dK/dV for 8 segments per (KV head, key block), plus
     # int32 tables per (batch, KV head): kept-item count and segment count per
-    # key block, and Tc/2 + 1 key-block pairs
+    # key block, Tc/2 + 1 key-block pairs, 8 work items per pair and a work
+    # count
     bh, tr = 2 * 4, 2
     part = 2 * 2 * 2 * 8 * 2 * 64 * 64 * 4  # B * Hkv * Tc * 8 * (dK, dV) * 64 * d * 4
-    tabs = 2 * 2 * (2 * 2 + 2 * (2 // 2 + 1)) * 4
+    tabs = 2 * 2 * (2 * 2 + 2 * 2 + 8 * 2 + 1) * 4
     want = a256(bh * tr * 1024) + a256(bh * tr * (tr + 1) // 2) + part + tabs
     assert L.mala_bwd_workspace_bytes(ctypes.byref(s), ctypes.byref(c)) == want
     s2 = shape(B=1, Hq=2, Hkv=1, Nq=130, Nk=700, d=128)
-    tabs = 1 * 1 * (2 * 11 + 2 * (11 // 2 + 1)) * 4
+    tabs = 1 * 1 * (2 * 11 + 2 * 6 + 8 * 6 + 1) * 4
     want = a256(2 * 3 * 1024) + a256(2 * 3 * 11) + 1 * 11 * 8 * 2 * 64 * 128 * 4 + tabs
     assert L.mala_bwd_workspace_bytes(ctypes.byref(s2), ctypes.byref(cfg(causal=0))) == want
     assert L.mala_bwd_workspace_bytes(ctypes.byref(shape(d=96)), ctypes.byref(c)) == 0
