@@ -277,6 +277,7 @@ __global__ __launch_bounds__(576, 1) void bwd_score_kernel(BwdParams p) {
         kreg[kt][dc] = ok ? *(const bf16x8*)(kbase + (size_t)key * D + 16 * dc + 8 * hh) : bf16x8{};
     }
     int kept = 0;
+    unsigned long long st_legal = 0, st_kept = 0, st_slots = 0;  // instrumentation
     for (int k = par; k < n_items; k += 2) {
       const int slot = k % RQ;
       wait_for([&] {
@@ -337,12 +338,10 @@ __global__ __launch_bounds__(576, 1) void bwd_score_kernel(BwdParams p) {
           const int bh = b * p.heads_q + item_h(k);
           p.dmap[dmap_index(p, bh, i, jw)] = want ? 1 : 0;
           if (kStats) {
-            if (p.counters) {
-              atomicAdd(&p.counters[0], 1ull);
-              if (want) {
-                atomicAdd(&p.counters[1], 1ull);
-                atomicAdd(&p.counters[2], (unsigned long long)min(64, p.nq - 64 * i) * 64ull);
-              }
+            ++st_legal;
+            if (want) {
+              ++st_kept;
+              st_slots += (unsigned long long)min(64, p.nq - 64 * i) * 64ull;
             }
             if (p.decisions) p.decisions[((size_t)bh * p.tr + i) * p.tc + jw] = want ? 1 : 0;
           }
@@ -354,6 +353,11 @@ __global__ __launch_bounds__(576, 1) void bwd_score_kernel(BwdParams p) {
         __hip_atomic_fetch_add(&done[slot], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     if (lane == 0) csum[w] = kept;
+    if (kStats && lane == 0 && p.counters) {
+      atomicAdd(&p.counters[0], st_legal);
+      atomicAdd(&p.counters[1], st_kept);
+      atomicAdd(&p.counters[2], st_slots);
+    }
   }
   lds_barrier();
   // kept items per key block (waves x and x + 4 score block x)
@@ -614,6 +618,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     return join_tr(h2[0], h2[1]);
   };
 
+  unsigned long long st_items = 0;  // instrumentation: kept (item, block) pairs listed
   for (int c0 = 0; c0 < n_items; c0 += CH) {
     const int nc = min(n_items - c0, CH);
 
@@ -630,7 +635,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
         const int bh = b * p.heads_q + h;
         if (legal(jA, i) && p.dmap[dmap_index(p, bh, i, jA)] != 0) mask |= 1;
         if (legal(jB, i) && p.dmap[dmap_index(p, bh, i, jB)] != 0) mask |= 2;
-        if (kStats && p.counters && mask) atomicAdd(&p.counters[3], (unsigned long long)__popc(mask));
+        if (kStats) st_items += __popc(mask);
       }
       const unsigned long long bal = __ballot(mask != 0);
       const int before = __popcll(bal & ((1ull << lane) - 1ull));
@@ -727,6 +732,11 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     }
   }
 
+  if (kStats && p.counters) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) st_items += __shfl_xor(st_items, off);
+    if (lane == 0 && st_items) atomicAdd(&p.counters[3], st_items);
+  }
   // ---- output: lane holds key 32 kh + l32 of block j, register 4e' + r of
   //      subtile dt = column 32 dt + 8e' + 4hh + r: dK = scale * sum and dV
   //      directly when the pair has one segment, else fp32 partials ----

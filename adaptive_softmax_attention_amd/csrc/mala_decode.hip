@@ -93,6 +93,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecParams p) {
       }
     };
     load_k(j_hi);
+    unsigned long long st_legal = 0, st_kept = 0, st_vtiles = 0;  // instrumentation
     for (int j = j_hi; j >= j_lo; --j) {
       floatx4 sc[4];
 #pragma unroll
@@ -121,18 +122,15 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecParams p) {
         want = col_ok;
       }
       if (col_ok && g4 == 0) {
-        if (kStats && p.counters) {
-          atomicAdd(&p.counters[0], 1ull);
-          if (want) {
-            atomicAdd(&p.counters[1], 1ull);
-            atomicAdd(&p.counters[2], 64ull);
-          }
+        if (kStats) {
+          ++st_legal;
+          if (want) ++st_kept;
         }
         if (kStats && p.decisions)
           p.decisions[(size_t)(b * p.heads_q + h0 + l16) * p.tc + j] = want ? 1 : 0;
       }
       if (!wave_any(want)) continue;  // no head retains: V tile never read
-      if (kStats && lane == 0 && p.counters) atomicAdd(&p.counters[3], 1ull);
+      if (kStats) ++st_vtiles;
 
       bf16x8 vr[KT];
 #pragma unroll
@@ -191,6 +189,19 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecParams p) {
         }
       }
       lds_barrier();
+    }
+    if (kStats && p.counters) {
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        st_legal += __shfl_xor(st_legal, off);
+        st_kept += __shfl_xor(st_kept, off);
+      }
+      if (lane == 0) {
+        atomicAdd(&p.counters[0], st_legal);
+        atomicAdd(&p.counters[1], st_kept);
+        atomicAdd(&p.counters[2], 64ull * st_kept);
+        atomicAdd(&p.counters[3], st_vtiles);
+      }
     }
   }
   // reduce the key phases, then write this split's partial (m, l, u)

@@ -249,6 +249,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   float mt = -INFINITY, alA = 1.f, alB = 1.f;
   bool pendA = false, pendB = false;  // P V outstanding for the tile in that set
   bool d_last = false;                // this block's decision on tile j+1
+  unsigned long long st_legal = 0, st_kept = 0, st_slots = 0, st_vtiles = 0;  // instrumentation
 
   issue_tile(kbase, jtop, k_lds + (jtop % RK) * kTileBytes, false);
   if (jtop >= 1) issue_tile(kbase, jtop - 1, k_lds + ((jtop - 1) % RK) * kTileBytes, false);
@@ -265,12 +266,10 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int x = 0; x < 8; ++x) any1 |= f[x];
       if (kStats && valid && jn <= jmax && half == 0 && lane == 0) {
-        if (p.counters) {
-          atomicAdd(&p.counters[0], 1ull);
-          if (d_last) {
-            atomicAdd(&p.counters[1], 1ull);
-            atomicAdd(&p.counters[2], (unsigned long long)vrows * 64ull);
-          }
+        ++st_legal;
+        if (d_last) {
+          ++st_kept;
+          st_slots += (unsigned long long)vrows * 64ull;
         }
         if (p.decisions)
           p.decisions[((size_t)(b * p.heads_q + h) * p.tr + i) * p.tc + jn] = d_last ? 1 : 0;
@@ -279,7 +278,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
     // V of tile j+1 only if some block retains it; then K two tiles ahead
     if (any1) {
       issue_tile(vbase, jn, v_lds + (jn % RV) * kTileBytes, true);
-      if (kStats && tid == 0 && p.counters) atomicAdd(&p.counters[3], 1ull);
+      if (kStats) ++st_vtiles;
     }
     if (j >= 2) issue_tile(kbase, j - 2, k_lds + ((j - 2) % RK) * kTileBytes, false);
 
@@ -338,6 +337,14 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
     if (j - 1 >= -2) step(j - 1, pB, alB, pendB);
   }
 
+  if (kStats && p.counters && lane == 0) {
+    if (half == 0 && valid) {
+      atomicAdd(&p.counters[0], st_legal);
+      atomicAdd(&p.counters[1], st_kept);
+      atomicAdd(&p.counters[2], st_slots);
+    }
+    if (w == 0) atomicAdd(&p.counters[3], st_vtiles);
+  }
   // ---- finalisation: O = O / l, LSE = m + log l ----
   if (row_ok) {
     const float inv = 1.f / lsum;

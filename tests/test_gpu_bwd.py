@@ -157,6 +157,11 @@ def compare_bwd(inp, tau, causal=True, sel_q=None, sel_k=None, fwd_sel=None, lab
         fm = fex["margin"][viol]
         assert np.all(np.abs(fm) < DELTA), "backward retained a tile forward skipped"
     out["bret"] = float((gd == 1).sum() / max(1, (gd >= 0).sum()))
+    # counters agree with the bitmaps: legal and kept tiles of the scoring pass, and
+    # every kept (tile, key block) listed once by the dK/dV pass
+    bc, fc = g["bcnt"], g["fcnt"]
+    assert bc[0] == int((gd >= 0).sum()) and bc[1] == int((gd == 1).sum()) and bc[3] == bc[1]
+    assert fc[0] == int((g["fdec"] >= 0).sum()) and fc[1] == int((g["fdec"] == 1).sum())
 
     # --- the backward alone, on the oracle's bf16-model forward outputs (the
     #     GPU's own outputs fill the rows the oracle did not compute; no
