@@ -9,9 +9,10 @@
  * the order the paper states them, OpenMP only across independent blocks.
  *
  * Sources (the paper "MassAlloc Attention: Let Attention Allocate Its Own
- * Compute", arXiv HTML 2609.32712, and the review "Why exact attention does not
- * need a quadratic matrix"):
- *   - tolerance tau/L_q and L_q = q+1 (causal) / N_k (decode): Sec. 2.1
+ * Compute" and the review "Why exact attention does not need a quadratic
+ * matrix"):
+ *   - tolerance tau/L_q and L_q = the keys query q sees (causal) / N_k
+ *     (decode): Sec. 2.1
  *   - online forward test, Eqs. (1)-(3), descending traversal: Sec. 2.2
  *   - forward procedure: Appendix A, Algorithm 1
  *   - offline backward test, Eq. (4): Sec. 2.2
@@ -25,6 +26,10 @@
  *   - the softmax scale is applied to Q.K inside (scores s = scale * <q,k>);
  *   - causal traversal starts at the last key block holding a legal key of the
  *     query block; non-causal starts at the last key block;
+ *   - causal with fewer queries than keys (prefill against a cache) aligns the
+ *     queries with the last keys: query q sits at position q + N_k - N_q, sees
+ *     keys k <= q + N_k - N_q, and L_q = q + N_k - N_q + 1 (the pages define
+ *     only N_q = N_k and single-token decode, which both cases reduce to);
  *   - a row constrains a forward tile only if it has a legal key in the tile;
  *   - skip is strict ("<"): a margin of exactly zero retains;
  *   - tau = 0 means log(tau/L) = -inf (never skip); tau = +inf means +inf;
@@ -89,15 +94,21 @@ static double round_bf16(double x) {
 
 static double round_f32(double x) { return (double)(float)x; }
 
+/* Position offset of the queries in causal problems: query q sits at key
+ * position q + N_k - N_q (0 when N_q = N_k). */
+static int64_t causal_offset(const orc_problem* p) {
+  return (int64_t)p->seqlen_k - (int64_t)p->seqlen_q;
+}
+
 static int legal(const orc_problem* p, int64_t q, int64_t k) {
   if (k < 0 || k >= p->seqlen_k) return 0;
-  if (p->causal && k > q) return 0;
+  if (p->causal && k > q + causal_offset(p)) return 0;
   return 1;
 }
 
 /* L_q: number of causally visible keys (Sec. 2.1). */
 static double visible(const orc_problem* p, int64_t q) {
-  return p->causal ? (double)(q + 1) : (double)p->seqlen_k;
+  return p->causal ? (double)(q + causal_offset(p) + 1) : (double)p->seqlen_k;
 }
 
 /* log(tau / L_q), with log 0 = -inf and tau = inf giving +inf. */
@@ -129,7 +140,7 @@ static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 static int64_t last_key_block(const orc_problem* p, int64_t q1) {
   int64_t tc = ceil_div(p->seqlen_k, p->block_k);
   if (!p->causal) return tc - 1;
-  int64_t last_key = q1 - 1;
+  int64_t last_key = q1 - 1 + causal_offset(p);
   if (last_key > p->seqlen_k - 1) last_key = p->seqlen_k - 1;
   return last_key / p->block_k;
 }

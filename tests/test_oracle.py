@@ -502,3 +502,115 @@ def test_magnitude_mode_equals_value_for_nonnegative_operands():
     bm = O.mala_bwd(q, k, v, r["o"], r["lse"], do, 1.0, True, 2, 2, round_flags=O.ABS,
                     force=b["dec"])
     assert np.allclose(bm["dv"], b["dv"], rtol=1e-13, atol=1e-13)
+
+
+# ------------------------------------------- causal with N_q < N_k (prefill) ----
+# Queries sit at the last N_q key positions (a chunk of prefill against a
+# cache): query q sees keys k <= q + N_k - N_q, and L_q counts them.
+
+def _rect_inputs(Nq, Nk, Hq, Hkv, d, seed):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((1, Hq, Nq, d)) * 1.5
+    k = rng.standard_normal((1, Hkv, Nk, d)) * 1.5
+    k[:, :, 0] += 2.0 * q.mean(axis=(1, 2))[:, None]
+    hubs = rng.choice(np.arange(1, Nk), size=2, replace=False)
+    k[:, :, hubs] *= 2.5
+    v = rng.standard_normal((1, Hkv, Nk, d))
+    do = rng.standard_normal((1, Hq, Nq, d))
+    return q, k, v, do
+
+
+@pytest.mark.parametrize("Nq,Nk,Hq,Hkv", [(5, 13, 2, 1), (16, 16, 2, 2), (1, 9, 2, 2), (7, 30, 4, 2)])
+def test_dense_bottom_right_matches_torch(Nq, Nk, Hq, Hkv):
+    d = 8
+    q, k, v, do = _rect_inputs(Nq, Nk, Hq, Hkv, d, 3)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = O.dense_fwd(q, k, v, True)
+    G = Hq // Hkv
+    tq = torch.tensor(q, requires_grad=True)
+    tk = torch.tensor(k, requires_grad=True)
+    tv = torch.tensor(v, requires_grad=True)
+    ke, ve = tk.repeat_interleave(G, dim=1), tv.repeat_interleave(G, dim=1)
+    allowed = torch.ones(Nq, Nk, dtype=torch.bool).tril(diagonal=Nk - Nq)  # bottom-right
+    to = torch.nn.functional.scaled_dot_product_attention(tq, ke, ve, attn_mask=allowed,
+                                                          scale=scale)
+    assert np.allclose(o, to.detach().numpy(), rtol=1e-12, atol=1e-12)
+    s = (tq @ ke.transpose(-1, -2)) * scale
+    tl = torch.logsumexp(s.masked_fill(~allowed, -math.inf), dim=-1)
+    assert np.allclose(lse, tl.detach().numpy(), rtol=1e-12, atol=1e-12)
+    to.backward(torch.tensor(do))
+    dq, dk, dv = O.dense_bwd(q, k, v, do, True)
+    for x, y in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        assert np.allclose(x, y.numpy(), rtol=1e-10, atol=1e-12)
+
+
+RECT = [
+    # (Nq, Nk, Hq, Hkv, d, bq, bk, tau)
+    (5, 13, 2, 1, 4, 2, 2, 1.0),
+    (7, 16, 2, 2, 4, 4, 2, 0.5),
+    (9, 14, 2, 1, 4, 2, 4, 2.0),
+    (1, 11, 2, 2, 4, 1, 3, 1.0),
+    (12, 16, 1, 1, 4, 4, 4, 4.0),
+]
+
+
+@pytest.mark.parametrize("case", RECT)
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_bottom_right_matches_bruteforce_twin(case, seed):
+    Nq, Nk, Hq, Hkv, d, bq, bk, tau = case
+    q, k, v, do = _rect_inputs(Nq, Nk, Hq, Hkv, d, seed)
+    r = O.mala_fwd(q, k, v, tau, True, bq, bk)
+    to, tl, tdec, _ = twin_fwd(q, k, v, tau, True, bq, bk)
+    assert not _near_zero(r["margin"]).any()
+    assert np.array_equal(r["dec"], tdec)
+    assert np.allclose(r["o"], to, rtol=1e-12, atol=1e-12)
+    assert np.allclose(r["lse"], tl, rtol=1e-12, atol=1e-12)
+    b = O.mala_bwd(q, k, v, r["o"], r["lse"], do, tau, True, bq, bk)
+    tq, tk, tv, tbd = twin_bwd(q, k, v, r["o"], r["lse"], do, tau, True, bq, bk)
+    assert not _near_zero(b["margin"]).any()
+    assert np.array_equal(b["dec"], tbd)
+    for x, y in ((b["dq"], tq), (b["dk"], tk), (b["dv"], tv)):
+        assert np.allclose(x, y, rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("off_blocks,bq,tau", [(1, 4, 1.0), (2, 4, 0.25), (3, 2, 4.0)])
+def test_bottom_right_is_the_suffix_of_the_full_problem(off_blocks, bq, tau):
+    """A chunk of N_q queries at the end of an N_k-token sequence is exactly the
+    last N_q rows of the full causal problem when N_k - N_q is a whole number
+    of query blocks (the blocks then coincide): same decisions, O and LSE, and
+    the same dQ; dK and dV equal the full backward with dO = 0 on the other
+    rows (those rows then contribute dS = 0)."""
+    Nq, d, bk, Hq, Hkv = 12, 4, 4, 2, 1
+    Nk = Nq + off_blocks * bq
+    q_full, k, v, do_full = _rect_inputs(Nk, Nk, Hq, Hkv, d, 7)
+    q_full *= 2.0  # more peaked scores, so that these small problems skip tiles
+    do_full[:, :, :Nk - Nq] = 0.0
+    q, do = q_full[:, :, Nk - Nq:], do_full[:, :, Nk - Nq:]
+    full = O.mala_fwd(q_full, k, v, tau, True, bq, bk)
+    part = O.mala_fwd(q, k, v, tau, True, bq, bk)
+    nb = off_blocks  # query blocks before the chunk
+    assert np.array_equal(part["dec"], full["dec"][:, :, nb:])
+    assert np.allclose(part["o"], full["o"][:, :, Nk - Nq:], rtol=1e-13, atol=1e-14)
+    assert np.allclose(part["lse"], full["lse"][:, :, Nk - Nq:], rtol=1e-13, atol=1e-14)
+    bf = O.mala_bwd(q_full, k, v, full["o"], full["lse"], do_full, tau, True, bq, bk)
+    bp = O.mala_bwd(q, k, v, part["o"], part["lse"], do, tau, True, bq, bk)
+    assert np.allclose(bp["dq"], bf["dq"][:, :, Nk - Nq:], rtol=1e-12, atol=1e-13)
+    assert np.allclose(bp["dk"], bf["dk"], rtol=1e-12, atol=1e-13)
+    assert np.allclose(bp["dv"], bf["dv"], rtol=1e-12, atol=1e-13)
+    assert (bp["dec"] == 0).any() or (part["dec"] == 0).any()  # the rule is exercised
+
+
+def test_single_causal_query_is_decode():
+    """One causal query at the end of the cache sees every key (L = N_k): it is
+    the one-split decode of that query (Sec. 2.4)."""
+    rng = np.random.default_rng(11)
+    Hq, Hkv, Nk, d, bk = 4, 2, 37, 4, 4
+    k = rng.standard_normal((1, Hkv, Nk, d)) * 1.5
+    k[:, :, [3, 20]] *= 2.5
+    v = rng.standard_normal((1, Hkv, Nk, d))
+    q = rng.standard_normal((1, Hq, 1, d)) * 1.5
+    for tau in (0.25, 1.0, 4.0):
+        f = O.mala_fwd(q, k, v, tau, True, 1, bk)
+        dd = O.mala_decode(q[:, :, 0], k, v, 1, tau, bk)
+        assert np.allclose(f["o"][:, :, 0], dd["o"], rtol=1e-13, atol=1e-14)
+        assert np.allclose(f["lse"][:, :, 0], dd["lse"], rtol=1e-13, atol=1e-14)

@@ -18,13 +18,14 @@ import numpy as np
 
 
 def _legal(Nq, Nk, causal):
-    qi = np.arange(Nq)[:, None]
+    # causal queries sit at the last Nq key positions: query q is at q + Nk - Nq
+    qi = np.arange(Nq)[:, None] + (Nk - Nq)
     kj = np.arange(Nk)[None, :]
     return (kj <= qi) if causal else np.ones((Nq, Nk), dtype=bool)
 
 
 def _visible(Nq, Nk, causal):
-    return (np.arange(Nq) + 1.0) if causal else np.full(Nq, float(Nk))
+    return (np.arange(Nq) + 1.0 + (Nk - Nq)) if causal else np.full(Nq, float(Nk))
 
 
 def twin_fwd_head(q, k, v, tau, causal, bq, bk, scale):
