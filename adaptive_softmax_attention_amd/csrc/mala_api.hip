@@ -74,7 +74,9 @@ int fwd_common(const mala_shape* shape, const mala_config* cfg, const void* q, c
   st = check_config(cfg, test);
   if (st) return st;
   if (!q || !k || !v || !o || !lse) return MALA_ERR_INVALID_ARG;
-  if (cfg->causal && shape->seqlen_q != shape->seqlen_k) return MALA_ERR_UNSUPPORTED;
+  // causal queries align with the last keys; more queries than keys would
+  // leave the first rows without a key
+  if (cfg->causal && shape->seqlen_q > shape->seqlen_k) return MALA_ERR_UNSUPPORTED;
   const int64_t tr = (shape->seqlen_q + 63) / 64;
   if ((int64_t)shape->batch * shape->heads_q * ((tr + 3) / 4 + 1) > kMaxGrid)
     return MALA_ERR_UNSUPPORTED;
@@ -109,7 +111,9 @@ int bwd_common(const mala_shape* shape, const mala_config* cfg, const void* q, c
   st = check_config(cfg, test);
   if (st) return st;
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return MALA_ERR_INVALID_ARG;
-  if (cfg->causal && shape->seqlen_q != shape->seqlen_k) return MALA_ERR_UNSUPPORTED;
+  // causal queries align with the last keys; more queries than keys would
+  // leave the first rows without a key
+  if (cfg->causal && shape->seqlen_q > shape->seqlen_k) return MALA_ERR_UNSUPPORTED;
   const size_t need = mala_bwd_workspace_bytes(shape, cfg);
   if (!workspace || workspace_bytes < need) return MALA_ERR_WORKSPACE;
   const int64_t tc = (shape->seqlen_k + 63) / 64;

@@ -64,6 +64,8 @@ struct BwdParams {
   float* part;     // [B*Hkv*Tc][kSegMax][2][64][D] fp32 partial dK, dV
   int batch, heads_q, heads_kv, nq, nk, group;
   int causal;
+  int off;   // causal: query q sits at key position q + off (off = nk - nq >= 0)
+  int cblk;  // causal: query block i reaches key block i + cblk, cblk = (63 + off) / 64
   float scale;
   float c;         // scale * log2(e): raw score -> log2 units
   float log2_tau;  // log2(tau); -inf for tau = 0, +inf for tau = inf
@@ -81,11 +83,37 @@ struct BwdParams {
   uint8_t* decisions;
 };
 
-// Decision byte of tile (i, j) of (batch, query head) bh: causal problems
-// store only the lower triangle.
+// Causal legal tiles: query block i reaches key blocks 0 .. min(tc - 1,
+// i + cblk), so the decision map stores min(tc, i + cblk + 1) bytes for it;
+// causal_row_start(i) is the number stored for the blocks before i (the
+// lower triangle when nq = nk).
+__host__ __device__ __forceinline__ long long causal_row_start(long long i, long long tc,
+                                                               long long cblk) {
+  const long long istar = tc - cblk - 1 > 0 ? tc - cblk - 1 : 0;  // blocks that reach every key block
+  const long long m = i < istar ? i : istar;
+  return m * (m - 1) / 2 + m * (cblk + 1) + (i - m) * tc;
+}
+
+// Decision byte of tile (i, j) of (batch, query head) bh.
 __device__ __forceinline__ long long dmap_index(const BwdParams& p, int bh, int i, int j) {
-  const long long t = p.causal ? (long long)i * (i + 1) / 2 + j : (long long)i * p.tc + j;
+  const long long t = p.causal ? causal_row_start(i, p.tc, p.cblk) + j : (long long)i * p.tc + j;
   return (long long)bh * p.dmap_per_head + t;
+}
+
+// causal: first query block with a legal key in key block j (its last row
+// 64 i + 63 reaches key 64 j: i >= (64 j - off - 63) / 64)
+__device__ __forceinline__ int first_qblock(const BwdParams& p, int j) {
+  if (!p.causal) return 0;
+  const int t = 64 * j - p.off;
+  return t > 0 ? min(p.tr - 1, t / 64) : 0;
+}
+// causal: key block j has a legal key for query block i
+__device__ __forceinline__ bool reaches(const BwdParams& p, int i, int j) {
+  return !p.causal || j <= i + p.cblk;
+}
+// causal: tile (i, j) holds a key beyond the limit of some row of block i
+__device__ __forceinline__ bool diag_tile(const BwdParams& p, int i, int j) {
+  return p.causal && 64 * j + 63 > 64 * i + p.off;
 }
 
 // MFMA row R of subtile x holds row 32(x/2) + 8(R/4) + 4(x%2) + R%4 of the
@@ -124,7 +152,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
     float* ri = p.rowinfo + blk * kRowInfo;
     if (valid) {
       const float z2 = p.lse[row] * kLog2e;
-      const float L = p.causal ? (float)(qq + 1) : (float)p.nk;  // visible keys
+      const float L = p.causal ? (float)(qq + p.off + 1) : (float)p.nk;  // visible keys
       ri[r] = z2;
       ri[64 + r] = (z2 + p.log2_tau - log2f(L)) / p.c;
       ri[128 + r] = acc;
@@ -190,7 +218,7 @@ __global__ __launch_bounds__(576, 1) void bwd_score_kernel(BwdParams p) {
   const int bk = (int)(blockIdx.x % per);
   const int b = bk / p.heads_kv, kvh = bk % p.heads_kv;
   const int jb0 = NB * G4;
-  const int i_lo = p.causal ? jb0 : 0;
+  const int i_lo = first_qblock(p, jb0);
   const int n_items = p.group * (p.tr - i_lo);
   auto item_i = [&](int it) { return p.tr - 1 - it / p.group; };
   auto item_h = [&](int it) { return kvh * p.group + it % p.group; };
@@ -285,10 +313,10 @@ __global__ __launch_bounds__(576, 1) void bwd_score_kernel(BwdParams p) {
                k + 1;
       });
       const int i = item_i(k);
-      if (live && (!p.causal || i >= jw)) {
+      if (live && reaches(p, i, jw)) {
         const char* qt = ring + slot * SQ;
         const float* wr = (const float*)(qt + TB);
-        const bool need_mask = (p.causal && i == jw) || (64 * jw + 64 > p.nk);
+        const bool need_mask = diag_tile(p, i, jw) || (64 * jw + 64 > p.nk);
         bool hit = false;
 #pragma unroll
         for (int qs = 0; qs < 2; ++qs) {
@@ -318,7 +346,7 @@ __global__ __launch_bounds__(576, 1) void bwd_score_kernel(BwdParams p) {
               for (int e = 0; e < 16; ++e) {
                 const int key = 64 * jw + 32 * kt + 8 * (e >> 2) + 4 * hh + (e & 3);
                 const int qq = 64 * i + 32 * qs + l32;
-                const bool ill = key >= p.nk || (p.causal && key > qq);
+                const bool ill = key >= p.nk || (p.causal && key > qq + p.off);
                 s[kt][e] = ill ? -INFINITY : s[kt][e];
               }
           }
@@ -395,7 +423,7 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdParams p) {
   const int* cnt = p.kcount + (size_t)bk * p.tc;
   int* pairs = p.pairs + (size_t)bk * p.npair * 2;
   auto heavy = [&](int j) {
-    const long long n = (long long)p.group * (p.tr - (p.causal ? j : 0));
+    const long long n = (long long)p.group * (p.tr - first_qblock(p, j));
     return 4ll * cnt[j] >= n;
   };
   for (int x = tid; x < 2 * p.npair; x += 256) pairs[x] = -1;
@@ -527,7 +555,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     jB = 2 * pr + 1 < p.tc ? 2 * pr + 1 : -1;
   }
   const int jlo = jB >= 0 ? min(jA, jB) : jA;
-  const int i_lo = p.causal ? jlo : 0;
+  const int i_lo = first_qblock(p, jlo);
   const int n_all = p.group * (p.tr - i_lo);
   if (seg == 0 && tid < 2 && p.segtab) {
     const int jx = tid ? jB : jA;
@@ -565,7 +593,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   const int n_items = min(n_all, it0 + seg_len) - it0;  // it0 .. it0 + n_items - 1
   auto item_i = [&](int it) { return p.tr - 1 - (it0 + it) / p.group; };
   auto item_h = [&](int it) { return kvh * p.group + (it0 + it) % p.group; };
-  auto legal = [&](int jx, int i) { return jx >= 0 && (!p.causal || i >= jx); };
+  auto legal = [&](int jx, int i) { return jx >= 0 && reaches(p, i, jx); };
 
   // ---- asynchronous tile copies: each wave moves a quarter of a tile and
   //      eight of the 32 row-term chunks ----
@@ -674,7 +702,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
       const __bf16* qt = (const __bf16*)(ring + (t % RP) * SP);
       const __bf16* dt_ = qt + 64 * D;
       const float* ri = (const float*)(qt + 2 * 64 * D);
-      const bool need_mask = (p.causal && i == j) || (64 * j + 64 > p.nk);
+      const bool need_mask = diag_tile(p, i, j) || (64 * j + 64 > p.nk);
 #pragma unroll
       for (int qs = 0; qs < 2; ++qs) {
         // S and dP for queries 32 qs .. 32 qs + 31: A = Q / dO rows
@@ -698,7 +726,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
 #pragma unroll
           for (int e2 = 0; e2 < 16; ++e2) {
             const int qq = 64 * i + 32 * qs + 8 * (e2 >> 2) + 4 * hh + (e2 & 3);
-            const bool ill = key >= p.nk || (p.causal && key > qq);
+            const bool ill = key >= p.nk || (p.causal && key > qq + p.off);
             s[e2] = ill ? -INFINITY : s[e2];
           }
         }
@@ -852,7 +880,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
   const bool valid = i < p.tr;
   const int q0 = 64 * i + 32 * half;
   const int i_top = min(ig * p.ipw + p.ipw - 1, p.tr - 1);
-  const int jtop = p.causal ? i_top : p.tc - 1;
+  const int jtop = p.causal ? min(p.tc - 1, i_top + p.cblk) : p.tc - 1;
   const size_t qrow0 = (size_t)(b * p.heads_q + h) * p.nq;
   const __bf16* kbase = p.k + (size_t)(b * p.heads_kv + kvh) * p.nk * D;
   const __bf16* vbase = p.v + (size_t)(b * p.heads_kv + kvh) * p.nk * D;
@@ -893,7 +921,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
   // one kept tile: S^T, dP^T, dS^T, dQ^T += K^T dS^T, one half of the 64
   // keys (key subtiles 2kc, 2kc + 1) at a time
   auto process = [&](const __bf16* kt, const __bf16* vt, int j) {
-    const bool need_mask = (p.causal && j == i) || (j * 64 + 64 > p.nk);
+    const bool need_mask = diag_tile(p, i, j) || (j * 64 + 64 > p.nk);
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
       floatx4 s[2][NQS], dp[2][NQS];
@@ -929,7 +957,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
             for (int r = 0; r < 4; ++r) {
               const int kk = j * 64 + qperm(2 * kc + x, 4 * g4 + r);
               const int qq = q0 + 16 * qs + l16;
-              if (kk >= p.nk || (p.causal && kk > qq)) s[x][qs][r] = -INFINITY;
+              if (kk >= p.nk || (p.causal && kk > qq + p.off)) s[x][qs][r] = -INFINITY;
             }
       }
       // dS^T = P^T (dP^T - D) as B operands [key][query]: keys 32kc + 8g4 + e
@@ -975,7 +1003,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           const int ix = blk_i(x);
-          if (ix >= p.tr || (p.causal && j > ix)) continue;
+          if (ix >= p.tr || !reaches(p, ix, j)) continue;
           const int bh = b * p.heads_q + blk_h(x);
           if (p.dmap[dmap_index(p, bh, ix, j)] != 0) mask |= 1 << x;
         }
@@ -1098,7 +1126,9 @@ size_t bwd_workspace_bytes(int batch, int heads_q, int heads_kv, int nq, int nk,
                            int causal) {
   const size_t tr = (size_t)(nq + 63) / 64, tc = (size_t)(nk + 63) / 64;
   const size_t rowinfo = (size_t)batch * heads_q * tr * kRowInfo * sizeof(float);
-  const size_t per_head = causal ? tr * (tr + 1) / 2 : tr * tc;
+  const long long off = causal ? (long long)nk - nq : 0;
+  const size_t per_head =
+      causal ? (size_t)causal_row_start((long long)tr, (long long)tc, (63 + off) / 64) : tr * tc;
   const size_t dmap = (size_t)batch * heads_q * per_head;
   const size_t part = (size_t)batch * heads_kv * tc * kSegMax * 2 * 64 * head_dim * sizeof(float);
   const size_t npair = tc / 2 + 1;
@@ -1124,12 +1154,14 @@ hipError_t launch_bwd(const BwdArgs& a, bool test, hipStream_t stream) {
   p.nk = a.nk;
   p.group = a.heads_q / a.heads_kv;
   p.causal = a.causal;
+  p.off = a.causal ? a.nk - a.nq : 0;
+  p.cblk = (63 + p.off) / 64;
   p.scale = a.scale;
   p.c = a.scale * kLog2e;
   p.log2_tau = a.tau == 0.f ? -INFINITY : log2f(a.tau);
   p.tr = (a.nq + 63) / 64;
   p.tc = (a.nk + 63) / 64;
-  p.dmap_per_head = p.causal ? (long long)p.tr * (p.tr + 1) / 2 : (long long)p.tr * p.tc;
+  p.dmap_per_head = p.causal ? causal_row_start(p.tr, p.tc, p.cblk) : (long long)p.tr * p.tc;
   const size_t rowinfo = (size_t)a.batch * a.heads_q * (size_t)p.tr * kRowInfo * sizeof(float);
   p.rowinfo = (float*)a.workspace;
   p.dmap = (uint8_t*)a.workspace + ((rowinfo + 255) & ~(size_t)255);

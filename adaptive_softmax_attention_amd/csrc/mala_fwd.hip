@@ -42,6 +42,8 @@ struct FwdParams {
   float* lse;
   int batch, heads_q, heads_kv, nq, nk;
   int causal;
+  int off;   // causal: query q sits at key position q + off (off = nk - nq >= 0)
+  int cblk;  // causal: query block i reaches key block i + cblk, cblk = (63 + off) / 64
   float c;         // softmax_scale * log2(e): raw score -> log2 units
   float log2_tau;  // log2(tau); -inf for tau = 0, +inf for tau = inf
   int group;       // heads_q / heads_kv
@@ -89,9 +91,11 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   const int i = ig * p.ipw + (blk / p.hpw);
   const bool valid = i < p.tr;
   const int qq = i * 64 + 32 * half + l32;  // the query column this lane holds
-  const int jmax = valid ? (p.causal ? i : p.tc - 1) : -1;
+  // last key block with a legal key for the block (causal: the block's last
+  // row sees up to key 64 i + 63 + off)
+  const int jmax = valid ? (p.causal ? min(p.tc - 1, i + p.cblk) : p.tc - 1) : -1;
   const int i_top = min(ig * p.ipw + p.ipw - 1, p.tr - 1);
-  const int jtop = p.causal ? i_top : p.tc - 1;
+  const int jtop = p.causal ? min(p.tc - 1, i_top + p.cblk) : p.tc - 1;
   const int vrows = valid ? min(64, p.nq - i * 64) : 0;
 
   const size_t qrow0 = (size_t)(b * p.heads_q + h) * p.nq;
@@ -99,7 +103,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   const __bf16* vbase = p.v + (size_t)(b * p.heads_kv + kvh) * p.nk * D;
 
   const bool row_ok = valid && qq < p.nq;
-  const float L = p.causal ? (float)(qq + 1) : (float)p.nk;  // visible keys
+  const float L = p.causal ? (float)(qq + p.off + 1) : (float)p.nk;  // visible keys
   const float thr = p.log2_tau - log2f(L);                    // log2(tau / L_q)
   float mref = -INFINITY, lsum = 0.f;
 
@@ -160,7 +164,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   // past 4hh is legal iff o <= lim
   auto mask = [&](floatx16 (&s)[2], int j) {
     int lim = p.nk - 1 - j * 64 - 4 * hh;
-    if (p.causal) lim = min(lim, qq - j * 64 - 4 * hh);
+    if (p.causal) lim = min(lim, qq + p.off - j * 64 - 4 * hh);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -287,7 +291,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
     bool dj = false;
     if (do_s) {
       score(&k_ring[0][0] + (j % RK) * 64 * D, sc);
-      if ((p.causal && j == i) || (j * 64 + 63 >= p.nk)) mask(sc, j);
+      if ((p.causal && j * 64 + 63 > i * 64 + p.off) || (j * 64 + 63 >= p.nk)) mask(sc, j);
       const bool mine = vote(sc, mt);
       if constexpr (kTest) {
         // publish this half's vote tagged with the tile, then wait for the
@@ -377,6 +381,8 @@ hipError_t launch_fwd(const FwdArgs& a, bool test, hipStream_t stream) {
   p.nq = a.nq;
   p.nk = a.nk;
   p.causal = a.causal;
+  p.off = a.causal ? a.nk - a.nq : 0;
+  p.cblk = (63 + p.off) / 64;
   p.c = a.scale * kLog2e;
   p.log2_tau = a.tau == 0.f ? -INFINITY : log2f(a.tau);
   p.group = a.heads_q / a.heads_kv;

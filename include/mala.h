@@ -2,8 +2,8 @@
  * mala.h - C ABI of the MassAlloc Attention (MALA) operator library for
  * AMD Instinct MI355X (gfx950).
  *
- * MALA ("MassAlloc Attention: Let Attention Allocate Its Own Compute",
- * arXiv HTML 2609.32712) is causal softmax attention that scores every legal
+ * MALA ("MassAlloc Attention: Let Attention Allocate Its Own Compute") is
+ * causal softmax attention that scores every legal
  * Q.K tile but runs the post-score work of a tile only when some valid query
  * row's normalised contribution reaches tau / L_q (Sec. 2.1; L_q = number of
  * keys the query sees). Forward tests against the running online-softmax
@@ -64,8 +64,13 @@ typedef struct {
 } mala_shape;
 
 typedef struct {
-  /* 1: causal with L_q = q + 1 (zero-based), requires seqlen_q == seqlen_k
-   *    (equal-length causal training, Sec. 2.1);
+  /* 1: causal. The queries are the last seqlen_q positions of the key
+   *    sequence: query q (zero-based) sees keys k <= q + seqlen_k - seqlen_q
+   *    and L_q = q + seqlen_k - seqlen_q + 1. seqlen_q == seqlen_k is
+   *    equal-length causal training (Sec. 2.1, L_q = q + 1); seqlen_q <
+   *    seqlen_k is prefill of a chunk against a cache (this library's reading;
+   *    the pages define the equal-length and single-token cases, which it
+   *    reduces to); seqlen_q > seqlen_k is rejected (MALA_ERR_UNSUPPORTED);
    * 0: every query sees all seqlen_k keys, L_q = seqlen_k. Ignored by
    *    decode, which always uses L = seqlen_k (Sec. 2.1, decoding). */
   int32_t causal;
@@ -99,7 +104,7 @@ typedef struct {
 
 /* MALA forward (Algorithm 1; Eqs. 1-3; the forward part of Appendix A.1).
  * Per (batch, query head, query block), key blocks holding a
- * legal key are visited from the last one (the diagonal when causal) down to
+ * legal key are visited from the last one (the shifted diagonal when causal) down to
  * block 0. Each tile is scored; it is skipped when every valid query row with
  * a legal key in it has rowmax - m - log l < log(tau / L_q); otherwise V is
  * loaded and every valid row of the block takes the online-softmax update.
@@ -115,7 +120,8 @@ int fullattn_fwd(const mala_shape* shape, const mala_config* cfg, const void* q,
 /* Bytes of device workspace mala_bwd / fullattn_bwd need: fp32 row terms
  * per 64-row query block (z = LSE in log2 units, the test threshold and
  * D = rowsum(O o dO); 1 KiB per block), one decision byte per legal tile
- * (the lower triangle when causal), and fp32 partial dK/dV sums for up to 8
+ * (when causal, query block i reaches key blocks 0 .. i + (63 + seqlen_k -
+ * seqlen_q) / 64), and fp32 partial dK/dV sums for up to 8
  * segments per 64-key block (8 x 2 x 64 x head_dim x 4 bytes per key block
  * and KV head: 512 KiB at head_dim 128), and int32 tables per (batch, KV
  * head): kept items and segments per key block, the Tc/2 + 1 key-block pairs

@@ -69,7 +69,7 @@ def fwd(s, c, q=FAKE, fn="mala_fwd"):
     (shape(), cfg(scale=float("inf")), m.MALA_ERR_INVALID_ARG),
     (shape(), cfg(scale=float("nan")), m.MALA_ERR_INVALID_ARG),
     (shape(), cfg(causal=2), m.MALA_ERR_INVALID_ARG),
-    (shape(Nq=100, Nk=128), cfg(causal=1), m.MALA_ERR_UNSUPPORTED),
+    (shape(Nq=128, Nk=100), cfg(causal=1), m.MALA_ERR_UNSUPPORTED),
     (shape(Nq=1 << 25, Nk=1 << 25), cfg(), m.MALA_ERR_UNSUPPORTED),
 ])
 def test_forward_validation(s, c, expect):
@@ -98,6 +98,8 @@ def _no_gpu():
 @pytest.mark.skipif(not _no_gpu(), reason="only meaningful where no GPU is visible")
 def test_valid_call_without_device_reports_device_error():
     assert fwd(shape(), cfg()) == m.MALA_ERR_DEVICE
+    # causal with fewer queries than keys (prefill against a cache) is accepted
+    assert fwd(shape(Nq=100, Nk=128), cfg()) == m.MALA_ERR_DEVICE
     assert fwd(shape(), cfg(tau=float("nan")), fn="fullattn_fwd") == m.MALA_ERR_DEVICE
 
 
@@ -106,7 +108,7 @@ def test_workspace_sizes():
     s, c = shape(B=2, Hq=4, Nq=100, Nk=100, d=64), cfg()
     a256 = lambda x: (x + 255) // 256 * 256
     # backward: 1 KiB of row terms per 64-row query block, plus one decision
-    # byte per legal tile (lower triangle when causal, Tr x Tc otherwise),
+    # byte per legal tile (lower triangle when causal and Nq = Nk, Tr x Tc when not causal),
     # plus fp32 partial dK/dV for 8 segments per (KV head, key block), plus
     # int32 tables per (batch, KV head): kept-item count and segment count per
     # key block, Tc/2 + 1 key-block pairs, 8 work items per pair and a work
@@ -120,6 +122,10 @@ def test_workspace_sizes():
     tabs = 1 * 1 * (2 * 11 + 2 * 6 + 8 * 6 + 1) * 4
     want = a256(2 * 3 * 1024) + a256(2 * 3 * 11) + 1 * 11 * 8 * 2 * 64 * 128 * 4 + tabs
     assert L.mala_bwd_workspace_bytes(ctypes.byref(s2), ctypes.byref(cfg(causal=0))) == want
+    # causal with the 130 queries at the end of 700 keys: query blocks 0, 1, 2
+    # reach key blocks 0..9, 0..10, 0..10 (32 decision bytes per head)
+    want = a256(2 * 3 * 1024) + a256(2 * 32) + 1 * 11 * 8 * 2 * 64 * 128 * 4 + tabs
+    assert L.mala_bwd_workspace_bytes(ctypes.byref(s2), ctypes.byref(cfg(causal=1))) == want
     assert L.mala_bwd_workspace_bytes(ctypes.byref(shape(d=96)), ctypes.byref(c)) == 0
     sd = shape(B=3, Hq=8, Hkv=2, Nq=1, Nk=1000, d=128)
     n = 3 * 8 * 5
@@ -137,7 +143,7 @@ def test_backward_validation():
     assert bwd(shape(), cfg(), ws=None) == m.MALA_ERR_WORKSPACE
     assert bwd(shape(), cfg(), nbytes=16) == m.MALA_ERR_WORKSPACE
     assert bwd(shape(), cfg(), dq=None) == m.MALA_ERR_INVALID_ARG
-    assert bwd(shape(Nq=64, Nk=128), cfg()) == m.MALA_ERR_UNSUPPORTED
+    assert bwd(shape(Nq=128, Nk=64), cfg()) == m.MALA_ERR_UNSUPPORTED
     assert bwd(shape(), cfg(tau=-2.0)) == m.MALA_ERR_INVALID_ARG
 
 

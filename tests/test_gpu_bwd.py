@@ -290,3 +290,17 @@ def test_cfg4_layout_8k_full():
     r = compare_bwd(inp, w.tau, label="cfg4-layout-8k")
     g = r["g"]
     assert g["dk"].abs().sum().item() > 0 and g["dv"].abs().sum().item() > 0
+
+
+@pytest.mark.parametrize("Nq,Nk,Hq,Hkv,d,tau", [
+    (37, 300, 4, 2, 128, 1.0),
+    (64, 300, 2, 1, 64, 0.25),
+    (256, 1024, 8, 1, 128, 1.0),
+    (129, 1000, 3, 3, 128, 4.0),
+])
+def test_backward_causal_chunk_against_cache(Nq, Nk, Hq, Hkv, d, tau):
+    """Backward of a causal chunk of the last Nq queries against Nk keys."""
+    a = W.peaked(W.Spec(950 + Nq, 1, Hq, Hkv, Nk, d, 3.0, 6))
+    inp = {"q": np.ascontiguousarray(a["q"][:, :, Nk - Nq:]), "k": a["k"], "v": a["v"],
+           "do": np.ascontiguousarray(a["do"][:, :, Nk - Nq:])}
+    compare_bwd(inp, tau, causal=True, label=f"chunk{Nq}of{Nk}")

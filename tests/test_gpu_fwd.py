@@ -188,3 +188,18 @@ def test_cfg4_forward_sampled():
     blocks = sorted(set([0, 1, Tr - 1, Tr // 2] + list(rng.integers(0, Tr, 6))))
     sel = [(0, int(h), int(i)) for i in blocks for h in (0, 5)]
     compare_fwd(inp, w.tau, sel=sel, label=w.name)
+
+
+@pytest.mark.parametrize("Nq,Nk,Hq,Hkv,d,tau", [
+    (1, 300, 4, 2, 128, 1.0),       # one query at the end of the cache
+    (37, 300, 4, 2, 128, 1.0),      # ragged chunk, offset not a whole tile
+    (64, 300, 2, 1, 64, 0.25),
+    (256, 1024, 8, 1, 128, 1.0),    # offset a whole number of tiles
+    (129, 1000, 3, 3, 128, 4.0),
+])
+def test_forward_causal_chunk_against_cache(Nq, Nk, Hq, Hkv, d, tau):
+    """Causal prefill of the last Nq queries against Nk keys (bottom-right
+    alignment: query q sees keys k <= q + Nk - Nq)."""
+    a = W.peaked(W.Spec(900 + Nq, 1, Hq, Hkv, Nk, d, 3.0, 6), want_do=False)
+    inp = {"q": np.ascontiguousarray(a["q"][:, :, Nk - Nq:]), "k": a["k"], "v": a["v"]}
+    compare_fwd(inp, tau, causal=True, label=f"chunk{Nq}of{Nk}")
