@@ -66,7 +66,7 @@ class Stats:
 
 EXPORTS = ("mala_fwd", "fullattn_fwd", "mala_bwd_workspace_bytes", "mala_bwd", "fullattn_bwd",
            "mala_decode_workspace_bytes", "mala_decode_default_splits", "mala_decode",
-           "fullattn_decode", "mala_status_string")
+           "fullattn_decode", "mala_decode_paged", "fullattn_decode_paged", "mala_status_string")
 
 _lib = None
 
@@ -93,6 +93,10 @@ def lib():
             getattr(L, f).restype = ctypes.c_int
         for f in ("mala_decode", "fullattn_decode"):
             getattr(L, f).argtypes = [ps, pc, vp, vp, vp, vp, vp, ctypes.c_int32, vp, sz, pst, vp]
+            getattr(L, f).restype = ctypes.c_int
+        for f in ("mala_decode_paged", "fullattn_decode_paged"):
+            getattr(L, f).argtypes = [ps, pc, vp, vp, vp, vp, vp, ctypes.c_int32, vp, vp,
+                                      ctypes.c_int32, vp, sz, pst, vp]
             getattr(L, f).restype = ctypes.c_int
         L.mala_bwd_workspace_bytes.argtypes = [ps, pc]
         L.mala_bwd_workspace_bytes.restype = sz
@@ -272,3 +276,52 @@ def fullattn_decode(q, k_cache, v_cache, o, lse, num_splits, workspace, *, block
     """Dense split-KV decode from the same kernels (test compiled out)."""
     _decode("fullattn_decode", q, k_cache, v_cache, o, lse, num_splits, workspace, 0.0, block_k,
             softmax_scale, stats, stream)
+
+
+def _decode_paged(name, q, k_pages, v_pages, block_table, cache_lens, max_len, o, lse,
+                  num_splits, workspace, tau, softmax_scale, stats, stream):
+    import torch
+    B, Hq, d = q.shape
+    P, Hkv = k_pages.shape[0], k_pages.shape[1]
+    _check(q, "q", torch.bfloat16, q.shape)
+    _check(k_pages, "k_pages", torch.bfloat16, (P, Hkv, 64, d))
+    _check(v_pages, "v_pages", torch.bfloat16, k_pages.shape)
+    _check(block_table, "block_table", torch.int32, (B, -(-int(max_len) // 64)))
+    _check(cache_lens, "cache_lens", torch.int32, (B,))
+    _check(o, "o", torch.bfloat16, q.shape)
+    _check(lse, "lse", torch.float32, (B, Hq))
+    if workspace is None or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace: a contiguous device tensor is required")
+    shp = Shape(B, Hq, Hkv, 1, int(max_len), d)
+    cfg = make_config(False, tau, 64, 64, softmax_scale, d)
+    st = stats._c() if stats is not None else None
+    nbytes = workspace.numel() * workspace.element_size()
+    rc = getattr(lib(), name)(ctypes.byref(shp), ctypes.byref(cfg), _ptr(q), _ptr(k_pages),
+                              _ptr(v_pages), _ptr(block_table), _ptr(cache_lens), int(P), _ptr(o),
+                              _ptr(lse), int(num_splits), _ptr(workspace), nbytes,
+                              ctypes.byref(st) if st is not None else None, _stream(stream))
+    if rc != MALA_OK:
+        raise MalaError(rc, name)
+
+
+def mala_decode_paged_workspace_bytes(q, max_len, heads_kv, num_splits):
+    B, Hq, d = q.shape
+    shp = Shape(B, Hq, int(heads_kv), 1, int(max_len), d)
+    return int(lib().mala_decode_workspace_bytes(ctypes.byref(shp), int(num_splits)))
+
+
+def mala_decode_paged(q, k_pages, v_pages, block_table, cache_lens, max_len, o, lse, num_splits,
+                      workspace, *, tau=1.0, softmax_scale=None, stats=None, stream=None):
+    """Split-KV MALA decode over a paged cache of variable-length sequences:
+    q/o [B,Hq,d] bf16, lse [B,Hq] fp32, pages [P,Hkv,64,d] bf16, block_table
+    [B, ceil(max_len/64)] int32, cache_lens [B] int32 (1..max_len), all on the
+    device."""
+    _decode_paged("mala_decode_paged", q, k_pages, v_pages, block_table, cache_lens, max_len, o,
+                  lse, num_splits, workspace, tau, softmax_scale, stats, stream)
+
+
+def fullattn_decode_paged(q, k_pages, v_pages, block_table, cache_lens, max_len, o, lse,
+                          num_splits, workspace, *, softmax_scale=None, stats=None, stream=None):
+    """Dense split-KV decode over the same paged cache."""
+    _decode_paged("fullattn_decode_paged", q, k_pages, v_pages, block_table, cache_lens, max_len,
+                  o, lse, num_splits, workspace, 0.0, softmax_scale, stats, stream)

@@ -156,7 +156,9 @@ int bwd_common(const mala_shape* shape, const mala_config* cfg, const void* q, c
 int decode_common(const mala_shape* shape, const mala_config* cfg, const void* q,
                   const void* k_cache, const void* v_cache, void* o, float* lse,
                   int32_t num_splits, void* workspace, size_t workspace_bytes,
-                  const mala_stats* stats, void* stream, bool test) {
+                  const mala_stats* stats, void* stream, bool test,
+                  const int32_t* block_table = nullptr, const int32_t* cache_lens = nullptr,
+                  int32_t num_pages = 0) {
   int st = check_shape(shape);
   if (st) return st;
   st = check_config(cfg, test);
@@ -192,6 +194,9 @@ int decode_common(const mala_shape* shape, const mala_config* cfg, const void* q
   a.tau = test ? cfg->tau : 0.f;
   a.counters = stats ? stats->counters : nullptr;
   a.decisions = stats ? stats->decisions : nullptr;
+  a.block_table = block_table;
+  a.cache_lens = cache_lens;
+  a.num_pages = num_pages;
   return launch_status(mala::launch_decode(a, test, (hipStream_t)stream));
 }
 
@@ -265,6 +270,26 @@ int fullattn_decode(const mala_shape* shape, const mala_config* cfg, const void*
                     const mala_stats* stats, void* stream) {
   return decode_common(shape, cfg, q, k_cache, v_cache, o, lse, num_splits, workspace,
                        workspace_bytes, stats, stream, false);
+}
+
+int mala_decode_paged(const mala_shape* shape, const mala_config* cfg, const void* q,
+                      const void* k_pages, const void* v_pages, const int32_t* block_table,
+                      const int32_t* cache_lens, int32_t num_pages, void* o, float* lse,
+                      int32_t num_splits, void* workspace, size_t workspace_bytes,
+                      const mala_stats* stats, void* stream) {
+  if (!block_table || !cache_lens || num_pages < 1) return MALA_ERR_INVALID_ARG;
+  return decode_common(shape, cfg, q, k_pages, v_pages, o, lse, num_splits, workspace,
+                       workspace_bytes, stats, stream, true, block_table, cache_lens, num_pages);
+}
+
+int fullattn_decode_paged(const mala_shape* shape, const mala_config* cfg, const void* q,
+                          const void* k_pages, const void* v_pages, const int32_t* block_table,
+                          const int32_t* cache_lens, int32_t num_pages, void* o, float* lse,
+                          int32_t num_splits, void* workspace, size_t workspace_bytes,
+                          const mala_stats* stats, void* stream) {
+  if (!block_table || !cache_lens || num_pages < 1) return MALA_ERR_INVALID_ARG;
+  return decode_common(shape, cfg, q, k_pages, v_pages, o, lse, num_splits, workspace,
+                       workspace_bytes, stats, stream, false, block_table, cache_lens, num_pages);
 }
 
 const char* mala_status_string(int status) {

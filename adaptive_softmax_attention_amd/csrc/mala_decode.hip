@@ -38,8 +38,16 @@ struct DecParams {
   float* part_l;
   float* part_u;
   int batch, heads_q, heads_kv, nk, group, splits, per, tc;
-  float c;    // softmax_scale * log2(e)
-  float thr;  // log2(tau / nk)
+  float c;         // softmax_scale * log2(e)
+  float thr;       // log2(tau / nk)
+  float log2_tau;  // log2(tau); -inf for tau = 0
+  // paged, variable-length cache (table == nullptr: one contiguous cache of
+  // nk keys per sequence): K / V pages [num_pages][heads_kv][64][D]; the
+  // keys 64 j .. 64 j + 63 of sequence b sit in page table[b * max_pages + j];
+  // sequence b holds lens[b] keys (1 <= lens[b] <= nk)
+  const int32_t* table;
+  const int32_t* lens;
+  int max_pages, num_pages;
   unsigned long long* counters;
   uint8_t* decisions;
 };
@@ -60,8 +68,22 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecParams p) {
   const int bk = blockIdx.x / p.splits;  // b * heads_kv + kvh
   const int b = bk / p.heads_kv, kvh = bk % p.heads_kv;
   const int h0 = kvh * p.group;
-  const int j_lo = s * p.per;
-  const int j_hi = min(p.tc, (s + 1) * p.per) - 1;
+  // this sequence's cache: its length, tiles, split range and tolerance
+  // (L = its own length); a length or page outside the cache makes the
+  // sequence's outputs NaN (no access outside the pages is made)
+  int nk = p.nk, tc = p.tc, per = p.per;
+  float thr = p.thr;
+  bool bad = false;
+  if (p.table) {
+    nk = p.lens[b];
+    bad = nk < 1 || nk > p.nk;
+    nk = bad ? 0 : nk;
+    tc = (nk + 63) / 64;
+    per = (tc + p.splits - 1) / p.splits;
+    thr = p.log2_tau - log2f((float)max(nk, 1));
+  }
+  const int j_lo = s * per;
+  const int j_hi = min(tc, (s + 1) * per) - 1;
   const bool col_ok = l16 < p.group;  // this lane's MFMA column is a real head
   const size_t prow = (size_t)(b * p.heads_q + h0 + l16) * p.splits + s;
 
@@ -73,8 +95,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecParams p) {
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
 
   if (j_lo <= j_hi) {
-    const __bf16* kbase = p.k + (size_t)bk * p.nk * D;
-    const __bf16* vbase = p.v + (size_t)bk * p.nk * D;
+    // row 0 of tile j of this sequence and KV head (nullptr: page out of range)
+    auto tile_k = [&](const __bf16* base, int j) -> const __bf16* {
+      if (!p.table) return base + ((size_t)bk * p.nk + (size_t)j * 64) * D;
+      const int pg = p.table[(size_t)b * p.max_pages + j];
+      if (pg < 0 || pg >= p.num_pages) return nullptr;
+      return base + ((size_t)pg * p.heads_kv + kvh) * 64 * D;
+    };
     // q^T as the B operand: column l16 = head h0 + l16
     bf16x8 qb[NDC];
 #pragma unroll
@@ -83,13 +110,16 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecParams p) {
                       : bf16x8{};
     bf16x8 kr[4][NDC];
     auto load_k = [&](int j) {
+      const __bf16* kt = tile_k(p.k, j);
+      bad = bad || kt == nullptr;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int key = j * 64 + 16 * ks + l16;
 #pragma unroll
         for (int dc = 0; dc < NDC; ++dc)
-          kr[ks][dc] = key < p.nk ? *(const bf16x8*)(kbase + (size_t)key * D + 32 * dc + 8 * g4)
-                                  : bf16x8{};
+          kr[ks][dc] = (kt && key < nk)
+                           ? *(const bf16x8*)(kt + (size_t)(16 * ks + l16) * D + 32 * dc + 8 * g4)
+                           : bf16x8{};
       }
     };
     load_k(j_hi);
@@ -110,14 +140,14 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int key = j * 64 + 16 * ks + 4 * g4 + r;
-          if (key >= p.nk) sc[ks][r] = -INFINITY;
+          if (key >= nk) sc[ks][r] = -INFINITY;
           mt = fmaxf(mt, sc[ks][r]);
         }
       mt = group4_max(mt);
       bool want;
       if constexpr (kTest) {
         // Eq. 3 for this head's single row, against the split's own (m, l)
-        want = col_ok && (lsum == 0.f || !(mt * p.c - m2 - fast_log2(lsum) - p.thr < 0.f));
+        want = col_ok && (lsum == 0.f || !(mt * p.c - m2 - fast_log2(lsum) - thr < 0.f));
       } else {
         want = col_ok;
       }
@@ -133,10 +163,12 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecParams p) {
       if (kStats) ++st_vtiles;
 
       bf16x8 vr[KT];
+      const __bf16* vt = tile_k(p.v, j);
 #pragma unroll
       for (int t = 0; t < KT; ++t) {
         const int key = j * 64 + kph + KPH * t;
-        vr[t] = key < p.nk ? *(const bf16x8*)(vbase + (size_t)key * D + 8 * dg) : bf16x8{};
+        vr[t] = (vt && key < nk) ? *(const bf16x8*)(vt + (size_t)(kph + KPH * t) * D + 8 * dg)
+                                 : bf16x8{};
       }
       // online-softmax update of the retaining heads
       float alpha = 1.f;
@@ -216,7 +248,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecParams p) {
     }
   if (col_ok && g4 == 0) {
     p.part_m[prow] = m2;
-    p.part_l[prow] = lsum;
+    p.part_l[prow] = bad ? NAN : lsum;
   }
   if (kph == 0) {
 #pragma unroll
@@ -239,8 +271,11 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecParams p) {
   const float* m = p.part_m + (size_t)row * p.splits;
   const float* l = p.part_l + (size_t)row * p.splits;
   float M = -INFINITY;
-  for (int s = 0; s < p.splits; ++s)
+  bool bad = false;  // a split met a length or page outside the cache
+  for (int s = 0; s < p.splits; ++s) {
     if (l[s] > 0.f) M = fmaxf(M, m[s]);
+    bad = bad || isnan(l[s]);
+  }
   float lt = 0.f, u = 0.f;
   for (int s = 0; s < p.splits; ++s) {
     if (!(l[s] > 0.f)) continue;
@@ -248,8 +283,8 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(DecParams p) {
     lt += w * l[s];
     u += w * p.part_u[((size_t)row * p.splits + s) * D + t];
   }
-  p.o[(size_t)row * D + t] = to_bf16(u / lt);
-  if (t == 0) p.lse[row] = (M + log2f(lt)) * kLn2;
+  p.o[(size_t)row * D + t] = to_bf16(bad ? NAN : u / lt);
+  if (t == 0) p.lse[row] = bad ? NAN : (M + log2f(lt)) * kLn2;
 }
 
 template <int D, int GM>
@@ -301,6 +336,11 @@ hipError_t launch_decode(const DecodeArgs& a, bool test, hipStream_t stream) {
   p.c = a.scale * kLog2e;
   const float log2_tau = a.tau == 0.f ? -INFINITY : log2f(a.tau);
   p.thr = log2_tau - log2f((float)a.nk);
+  p.log2_tau = log2_tau;
+  p.table = a.block_table;
+  p.lens = a.cache_lens;
+  p.max_pages = p.tc;
+  p.num_pages = a.num_pages;
   p.counters = a.counters;
   p.decisions = a.decisions;
   if (p.group > 8) return hipErrorNotSupported;

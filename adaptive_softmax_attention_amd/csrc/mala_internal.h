@@ -54,6 +54,10 @@ struct DecodeArgs {
   float tau;
   unsigned long long* counters;
   uint8_t* decisions;
+  // paged, variable-length cache (nullptr: contiguous caches of nk keys)
+  const int32_t* block_table;  // [batch][ceil(nk / 64)]
+  const int32_t* cache_lens;   // [batch]
+  int num_pages;
 };
 
 // Each returns hipSuccess or the launch error. `test` selects the MALA rule

@@ -181,6 +181,35 @@ int fullattn_decode(const mala_shape* shape, const mala_config* cfg, const void*
                     int32_t num_splits, void* workspace, size_t workspace_bytes,
                     const mala_stats* stats, void* stream);
 
+/* Split-KV decode over a paged cache of variable-length sequences (the MALA
+ * paper's Sec. 2.4 and the decoding part of its Appendix A.1; the serving
+ * layout is this library's). Sequence b holds cache_lens[b] keys (1 <= cache_lens[b] <=
+ * shape->seqlen_k) and its own tolerance tau / cache_lens[b] (L = its own
+ * cache length, Sec. 2.1). Its keys 64 j .. 64 j + 63 sit in page
+ * block_table[b * ceil(seqlen_k / 64) + j] of k_pages / v_pages, each page
+ * [heads_kv][64][head_dim] bf16 (pages [num_pages][heads_kv][64][head_dim]).
+ * block_table (int32 [batch][ceil(seqlen_k / 64)]) and cache_lens (int32
+ * [batch]) are device arrays; only the first ceil(cache_lens[b] / 64) entries
+ * of a row are read. Each sequence's ceil(cache_lens[b] / 64) tiles are cut
+ * into num_splits ranges as in mala_decode (splits past a short cache are
+ * empty). q, o, lse, num_splits, workspace (mala_decode_workspace_bytes) and
+ * stats as for mala_decode; shape->seqlen_q must be 1. A cache length or page
+ * index out of range is not read from: that sequence's o and lse become NaN,
+ * the others are unaffected. Returns MALA_ERR_INVALID_ARG for null tables or
+ * num_pages < 1, else as mala_decode. */
+int mala_decode_paged(const mala_shape* shape, const mala_config* cfg, const void* q,
+                      const void* k_pages, const void* v_pages, const int32_t* block_table,
+                      const int32_t* cache_lens, int32_t num_pages, void* o, float* lse,
+                      int32_t num_splits, void* workspace, size_t workspace_bytes,
+                      const mala_stats* stats, void* stream);
+
+/* Dense split-KV decode over the same paged cache (tau ignored). */
+int fullattn_decode_paged(const mala_shape* shape, const mala_config* cfg, const void* q,
+                          const void* k_pages, const void* v_pages, const int32_t* block_table,
+                          const int32_t* cache_lens, int32_t num_pages, void* o, float* lse,
+                          int32_t num_splits, void* workspace, size_t workspace_bytes,
+                          const mala_stats* stats, void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* mala_status_string(int status);
 

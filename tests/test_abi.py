@@ -26,7 +26,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     L = m.lib()
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 12
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(m.EXPORTS)
@@ -168,3 +168,19 @@ def test_binding_rejects_bad_tensors():
     q = torch.zeros(1, 2, 64, 64, dtype=torch.float32)
     with pytest.raises(ValueError):
         m.mala_fwd(q, q, q, q, q[..., 0])
+
+
+def test_decode_paged_validation():
+    L = m.lib()
+    s = shape(Nq=1, Nk=4096)
+
+    def call(table=FAKE, lens=FAKE, pages=8, S=4, fn="mala_decode_paged"):
+        return getattr(L, fn)(ctypes.byref(s), ctypes.byref(cfg(causal=0)), FAKE, FAKE, FAKE,
+                              table, lens, pages, FAKE, FAKE, S, FAKE, 1 << 40, None, None)
+    assert call(table=None) == m.MALA_ERR_INVALID_ARG
+    assert call(lens=None) == m.MALA_ERR_INVALID_ARG
+    assert call(pages=0) == m.MALA_ERR_INVALID_ARG
+    assert call(S=0) == m.MALA_ERR_INVALID_ARG
+    assert call(table=None, fn="fullattn_decode_paged") == m.MALA_ERR_INVALID_ARG
+    if _no_gpu():
+        assert call() == m.MALA_ERR_DEVICE

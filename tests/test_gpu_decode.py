@@ -134,3 +134,133 @@ def test_cfg5_full_cache_sampled(variant):
     r = compare_decode(decode_inputs(w.spec), 1.0, w.extra["num_splits"], batches=[0, 15],
                        label=w.name)
     print("retained head-tiles", r["cnt"][1] / r["cnt"][0], "V tiles", r["cnt"][3])
+
+
+# ---- paged cache of variable-length sequences (mala_decode_paged) ----
+
+def paged_inputs(seed, lens, Hq, Hkv, d, spare=5):
+    """Caches of len(lens) sequences from the generator (sequence b keeps its
+    first lens[b] keys; its query is its row lens[b] - 1), stored in 64-key
+    pages at shuffled page indices, with spare pages of noise."""
+    B, max_len = len(lens), max(lens)
+    inp = W.peaked(W.Spec(seed, B, Hq, Hkv, max_len, d, 3.0, 8), want_do=False)
+    q = np.stack([inp["q"][b, :, lens[b] - 1] for b in range(B)])
+    tiles = [-(-n // 64) for n in lens]
+    P = sum(tiles) + spare
+    rng = np.random.default_rng(seed)
+    order = rng.permutation(P)
+    noise = W.f32_to_bf16_bits(rng.standard_normal((P, Hkv, 64, d)).astype(np.float32))
+    kp, vp = noise.copy(), noise.copy()
+    table = np.zeros((B, -(-max_len // 64)), dtype=np.int32)
+    t = 0
+    for b in range(B):
+        for j in range(tiles[b]):
+            pg = int(order[t])
+            t += 1
+            table[b, j] = pg
+            rows = slice(64 * j, min(64 * j + 64, lens[b]))
+            n = rows.stop - rows.start
+            kp[pg, :, :n] = inp["k"][b, :, rows]
+            vp[pg, :, :n] = inp["v"][b, :, rows]
+    return {"q": q, "k": inp["k"], "v": inp["v"], "kp": kp, "vp": vp, "table": table,
+            "lens": np.array(lens, dtype=np.int32), "max_len": max_len}
+
+
+def run_decode_paged(pin, tau, S, dense=False, lens=None):
+    m = mala()
+    q = bits_to_gpu(pin["q"])
+    kp, vp = bits_to_gpu(pin["kp"]), bits_to_gpu(pin["vp"])
+    table = torch.from_numpy(pin["table"]).cuda()
+    lens_g = torch.from_numpy(pin["lens"] if lens is None else lens).cuda()
+    B, Hq, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    ws = torch.empty(m.mala_decode_paged_workspace_bytes(q, pin["max_len"], kp.shape[1], S),
+                     dtype=torch.uint8, device="cuda")
+    st = m.Stats(torch.zeros(4, dtype=torch.int64, device="cuda"),
+                 torch.full((B, Hq, table.shape[1]), 255, dtype=torch.uint8, device="cuda"))
+    if dense:
+        m.fullattn_decode_paged(q, kp, vp, table, lens_g, pin["max_len"], o, lse, S, ws, stats=st)
+    else:
+        m.mala_decode_paged(q, kp, vp, table, lens_g, pin["max_len"], o, lse, S, ws, tau=tau,
+                            stats=st)
+    torch.cuda.synchronize()
+    return o, lse, st.decisions.cpu().numpy().astype(np.int8), st.counters.cpu().numpy()
+
+
+@pytest.mark.parametrize("tau,S", [(1.0, 3), (0.0, 2), (4.0, 1)])
+def test_decode_paged_varlen(tau, S):
+    """Each sequence against the oracle's decode of its own cache (its own
+    L = cache length), with the same decision, V1/V2 and LSE checks."""
+    lens = [1, 63, 64, 700, 1000]
+    pin = paged_inputs(41, lens, 8, 2, 128)
+    o, lse, dec, cnt = run_decode_paged(pin, tau, S)
+    go, gl = gpu_to_f64(o), lse.cpu().numpy().astype(np.float64)
+    assert np.isfinite(go).all() and np.isfinite(gl).all()
+    legal_total = kept_total = 0
+    for b, n in enumerate(lens):
+        q = bits_to_f64(pin["q"][b:b + 1])
+        k = bits_to_f64(pin["k"][b:b + 1, :, :n])
+        v = bits_to_f64(pin["v"][b:b + 1, :, :n])
+        nt = -(-n // 64)
+        gd = dec[b:b + 1, :, :nt]
+        assert (dec[b, :, nt:] == -1).all()  # tiles past the sequence are never tested
+
+        def run(force, flags=O.EXACT):
+            return O.mala_decode(q, k, v, S, tau, 64, round_flags=flags, force=force)
+
+        free = run(None)
+        legal = free["dec"] >= 0
+        check_decisions(gd, free, legal)
+        ex, _ = settle_fwd_branch(run, gd, legal, free=free)
+        bf = run(ex["dec"].copy(), O.BF16_DECODE)
+        mag = run(ex["dec"].copy(), O.BF16_DECODE | O.ABS)
+        ok, worst = v1_ok(go[b:b + 1], bf["o"], mag["o"])
+        assert ok, f"sequence {b}: V1 worst ratio {worst}"
+        assert v2(go[b:b + 1], bf["o"]) <= V2_TOL
+        assert np.abs(gl[b:b + 1] - ex["lse"]).max() <= LSE_TOL
+        legal_total += int(legal.sum())
+        kept_total += int((gd == 1).sum())
+    assert cnt[0] == legal_total and cnt[1] == kept_total
+
+
+def test_decode_paged_equals_contiguous():
+    """Equal lengths and pages in order: the paged path computes exactly what
+    mala_decode computes on the contiguous caches (bitwise), MALA and dense."""
+    m = mala()
+    spec = W.Spec(43, 3, 8, 2, 777, 128, 3.0, 8)
+    inp = decode_inputs(spec)
+    B, Hkv, N, d = inp["k"].shape
+    T = -(-N // 64)
+    kp = np.zeros((B * T, Hkv, 64, d), dtype=np.uint16)
+    vp = np.zeros_like(kp)
+    table = np.zeros((B, T), dtype=np.int32)
+    for b in range(B):
+        for j in range(T):
+            rows = slice(64 * j, min(64 * j + 64, N))
+            kp[b * T + j, :, :rows.stop - rows.start] = inp["k"][b, :, rows]
+            vp[b * T + j, :, :rows.stop - rows.start] = inp["v"][b, :, rows]
+            table[b, j] = b * T + j
+    pin = {"q": inp["q"], "kp": kp, "vp": vp, "table": table,
+           "lens": np.full(B, N, dtype=np.int32), "max_len": N}
+    for dense in (False, True):
+        o1, l1, _, _ = run_decode(inp, 1.0, 4, dense=dense)
+        o2, l2, _, _ = run_decode_paged(pin, 1.0, 4, dense=dense)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_decode_paged_bad_entries_give_nan_for_that_sequence():
+    """A cache length or page index out of range is never read from: that
+    sequence's outputs become NaN and the others keep their values."""
+    lens = [100, 300, 200]
+    pin = paged_inputs(47, lens, 4, 2, 128)
+    o_ref, l_ref, _, _ = run_decode_paged(pin, 1.0, 2)
+    bad_lens = np.array([100, 300 + 10 ** 6, 200], dtype=np.int32)  # sequence 1: too long
+    o, l, _, _ = run_decode_paged(pin, 1.0, 2, lens=bad_lens)
+    assert torch.isnan(o[1].float()).all() and torch.isnan(l[1]).all()
+    assert torch.equal(o[0], o_ref[0]) and torch.equal(o[2], o_ref[2])
+    pin2 = dict(pin, table=pin["table"].copy())
+    pin2["table"][2, 1] = 10 ** 6  # sequence 2: page index past the pages
+    o, l, _, _ = run_decode_paged(pin2, 1.0, 2)
+    assert torch.isnan(o[2].float()).all() and torch.isnan(l[2]).all()
+    assert torch.equal(o[0], o_ref[0]) and torch.equal(o[1], o_ref[1])
