@@ -25,6 +25,8 @@ applied independently to every (batch b, KV head g) with G = Hq / Hkv:
    [Bk + 1, N), query head g*G + (t mod G), distinct key positions p'_t in
    [1, p_t - Bk]; K[p'_t] = 4 Q[h_t, p_t].
 5. V ~ N(0, 1), dO ~ N(0, 1).
+   (optional head_gain = (lo, hi)) after the planting, every query head h of
+   entry b is multiplied by its own gain, log-uniform in [lo, hi].
 6. every tensor is rounded once fp32 -> bf16 (round to nearest even).
 
 Random streams: numpy PCG64 seeded by SeedSequence(seed, spawn_key=(b, head,
@@ -42,7 +44,7 @@ import numpy as np
 
 Q_CHUNK = 64
 KV_CHUNK = 4096
-_TID_Q, _TID_K, _TID_V, _TID_DO, _TID_U, _TID_PLANT = range(6)
+_TID_Q, _TID_K, _TID_V, _TID_DO, _TID_U, _TID_PLANT, _TID_GAIN = range(7)
 
 
 def _rng(seed, b, head, tid, chunk=0):
@@ -100,6 +102,7 @@ class Spec:
     n_planted: int = 0
     local_bias: bool = False
     block_k: int = 64
+    head_gain: tuple | None = None
 
     @property
     def group(self):
@@ -132,6 +135,16 @@ def _planted(spec: Spec, b, g):
         used.add(kp)
         out.append((int(p), g * G + (t % G), kp))
     return np.asarray(out, dtype=np.int64).reshape(-1, 3)
+
+
+def head_gain(spec: Spec, b: int, h: int) -> float:
+    """Query gain of head h of batch entry b (1 unless spec.head_gain = (lo, hi)):
+    log-uniform in [lo, hi], one draw per (b, h)."""
+    if spec.head_gain is None:
+        return 1.0
+    lo, hi = spec.head_gain
+    x = _rng(spec.seed, b, h, _TID_GAIN).random()
+    return math.exp(math.log(lo) + x * (math.log(hi) - math.log(lo)))
 
 
 def _group(spec: Spec, b: int, g: int, q_rows, want_do: bool):
@@ -177,6 +190,9 @@ def _group(spec: Spec, b: int, g: int, q_rows, want_do: bool):
             qrow = _normal_rows(spec.seed, b, h, _TID_Q, np.array([p]), d, Q_CHUNK, sig_e)[0]
             qrow = qrow + np.float32(2.0 * sig_e) * u
         k[kp] = np.float32(4.0) * qrow
+    if spec.head_gain is not None:
+        for h in heads:
+            q[h] *= np.float32(head_gain(spec, b, h))
     v = _normal_full(spec.seed, b, g, _TID_V, N, d, KV_CHUNK)
     do = None
     if want_do:
@@ -310,3 +326,19 @@ def cfg5(variant: str = "peaked", tau: float = 1.0, num_splits: int = 16):
 
 
 DECODE_TAUS = (0.0, 0.25, 1.0, 4.0)
+
+
+MATCHED_WORK_VARIANTS = ("uniform", "mixed")
+
+
+def matched_work(variant: str = "uniform"):
+    """Matched-work allocation study at 8K: B 4 independent inputs (each batch
+    entry draws its own streams), 16 query / 4 KV heads, d 128, 64 planted,
+    local bias. "mixed" also scales each (input, query head) by its own query
+    gain, log-uniform in [0.5, 2], so that heads and inputs differ in
+    sharpness; "uniform" draws them all alike."""
+    if variant == "uniform":
+        spec = Spec(601, 4, 16, 4, 8192, 128, 3.0, 64, local_bias=True)
+    else:
+        spec = Spec(602, 4, 16, 4, 8192, 128, 3.0, 64, local_bias=True, head_gain=(0.5, 2.0))
+    return Workload(f"matched_work_8k_b4_gqa16x4_d128_{variant}", spec, passes=("fwd",))
