@@ -66,6 +66,15 @@ int launch_status(hipError_t e) { return e == hipSuccess ? MALA_OK : MALA_ERR_LA
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// The kernels move bf16 rows in 16-byte vectors and the workspace in float4
+// words; lse, tables and lengths are read as 4-byte words, counters as
+// 8-byte atomics.
+bool aligned(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
+
+bool stats_aligned(const mala_stats* stats) {
+  return !stats || !stats->counters || aligned(stats->counters, 8);
+}
+
 int fwd_common(const mala_shape* shape, const mala_config* cfg, const void* q, const void* k,
                const void* v, void* o, float* lse, const mala_stats* stats, void* stream,
                bool test) {
@@ -74,6 +83,9 @@ int fwd_common(const mala_shape* shape, const mala_config* cfg, const void* q, c
   st = check_config(cfg, test);
   if (st) return st;
   if (!q || !k || !v || !o || !lse) return MALA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4) || !stats_aligned(stats))
+    return MALA_ERR_INVALID_ARG;
   // causal queries align with the last keys; more queries than keys would
   // leave the first rows without a key
   if (cfg->causal && shape->seqlen_q > shape->seqlen_k) return MALA_ERR_UNSUPPORTED;
@@ -111,11 +123,16 @@ int bwd_common(const mala_shape* shape, const mala_config* cfg, const void* q, c
   st = check_config(cfg, test);
   if (st) return st;
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return MALA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 4) || !stats_aligned(stats))
+    return MALA_ERR_INVALID_ARG;
   // causal queries align with the last keys; more queries than keys would
   // leave the first rows without a key
   if (cfg->causal && shape->seqlen_q > shape->seqlen_k) return MALA_ERR_UNSUPPORTED;
   const size_t need = mala_bwd_workspace_bytes(shape, cfg);
   if (!workspace || workspace_bytes < need) return MALA_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return MALA_ERR_INVALID_ARG;
   const int64_t tc = (shape->seqlen_k + 63) / 64;
   const int64_t tr = (shape->seqlen_q + 63) / 64;
   // the dK/dV pass launches up to 8 segment workgroups per key block
@@ -165,12 +182,17 @@ int decode_common(const mala_shape* shape, const mala_config* cfg, const void* q
   if (st) return st;
   if (shape->seqlen_q != 1) return MALA_ERR_INVALID_ARG;
   if (!q || !k_cache || !v_cache || !o || !lse) return MALA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4) || !aligned(block_table, 4) || !aligned(cache_lens, 4) ||
+      !stats_aligned(stats))
+    return MALA_ERR_INVALID_ARG;
   if (shape->heads_q / shape->heads_kv > 8) return MALA_ERR_UNSUPPORTED;
   if (num_splits < 1) return MALA_ERR_INVALID_ARG;
   const int64_t tc = (shape->seqlen_k + 63) / 64;
   if (num_splits > tc) return MALA_ERR_INVALID_ARG;  // every split owns >= 1 tile
   const size_t need = mala_decode_workspace_bytes(shape, num_splits);
   if (!workspace || workspace_bytes < need) return MALA_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return MALA_ERR_INVALID_ARG;
   if ((int64_t)shape->batch * shape->heads_kv * num_splits > kMaxGrid) return MALA_ERR_UNSUPPORTED;
   st = check_device();
   if (st) return st;

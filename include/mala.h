@@ -24,6 +24,11 @@
  *       LSE            [batch][heads_q ][seqlen_q]            fp32
  *     LSE holds z_q = log Z_R,q, the natural log of the retained normaliser
  *     of the scaled scores (Sec. 2.2, end of "Online Sparse Softmax").
+ *   - Alignment: the bf16 tensors (Q, K, V, O, dO, dQ, dK, dV, K/V pages)
+ *     and the workspace start on 16-byte boundaries; LSE, block tables and
+ *     cache lengths on 4-byte boundaries; stats counters on 8-byte
+ *     boundaries. hipMalloc and PyTorch allocations satisfy all of these;
+ *     a misaligned pointer returns MALA_ERR_INVALID_ARG.
  *   - Query head h reads KV head h / (heads_q / heads_kv) (grouped-query
  *     attention; heads_q must be a multiple of heads_kv).
  *   - head_dim is 64 or 128. The decision tile is block_q x block_k; this
@@ -47,7 +52,7 @@ extern "C" {
 
 typedef enum {
   MALA_OK = 0,
-  MALA_ERR_INVALID_ARG = 1, /* null pointer, bad size, bad tau/scale, ... */
+  MALA_ERR_INVALID_ARG = 1, /* null or misaligned pointer, bad size, bad tau/scale, ... */
   MALA_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim, tile size */
   MALA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
   MALA_ERR_DEVICE = 4,      /* no usable HIP device / wrong architecture */

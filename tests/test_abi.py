@@ -184,3 +184,47 @@ def test_decode_paged_validation():
     assert call(table=None, fn="fullattn_decode_paged") == m.MALA_ERR_INVALID_ARG
     if _no_gpu():
         assert call() == m.MALA_ERR_DEVICE
+
+
+MIS = ctypes.c_void_p(0x1002)  # 2-byte aligned: below what every tensor needs
+
+
+def test_misaligned_pointers_are_rejected():
+    L = m.lib()
+    s, c = shape(), cfg()
+    # forward: any bf16 tensor off a 16-byte boundary, or lse off 4 bytes
+    for pos in range(4):
+        args = [FAKE] * 4
+        args[pos] = MIS
+        assert L.mala_fwd(ctypes.byref(s), ctypes.byref(c), *args, FAKE, None, None) == \
+            m.MALA_ERR_INVALID_ARG, pos
+    assert L.mala_fwd(ctypes.byref(s), ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, MIS, None,
+                      None) == m.MALA_ERR_INVALID_ARG
+    assert L.fullattn_fwd(ctypes.byref(s), ctypes.byref(c), MIS, FAKE, FAKE, FAKE, FAKE, None,
+                          None) == m.MALA_ERR_INVALID_ARG
+    # counters must be 8-byte aligned
+    st = m._CStats(0x1004, None)
+    assert L.mala_fwd(ctypes.byref(s), ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE,
+                      ctypes.byref(st), None) == m.MALA_ERR_INVALID_ARG
+    # backward: each of the nine tensors, then the workspace
+    for pos in range(9):
+        args = [FAKE] * 9
+        args[pos] = MIS
+        assert L.mala_bwd(ctypes.byref(s), ctypes.byref(c), *args, FAKE, 1 << 40, None,
+                          None) == m.MALA_ERR_INVALID_ARG, pos
+    assert L.mala_bwd(ctypes.byref(s), ctypes.byref(c), *([FAKE] * 9), ctypes.c_void_p(0x1008),
+                      1 << 40, None, None) == m.MALA_ERR_INVALID_ARG
+    # decode: q, caches, o, lse, workspace
+    sd = shape(Nq=1, Nk=4096)
+    for pos in range(5):
+        args = [FAKE] * 5
+        args[pos] = MIS
+        assert L.mala_decode(ctypes.byref(sd), ctypes.byref(c), *args, 4, FAKE, 1 << 40, None,
+                             None) == m.MALA_ERR_INVALID_ARG, pos
+    assert L.mala_decode(ctypes.byref(sd), ctypes.byref(c), *([FAKE] * 5), 4,
+                         ctypes.c_void_p(0x1008), 1 << 40, None, None) == m.MALA_ERR_INVALID_ARG
+    # paged: block table and lengths are int32 words
+    for table, lens in ((MIS, FAKE), (FAKE, MIS)):
+        assert L.mala_decode_paged(ctypes.byref(sd), ctypes.byref(cfg(causal=0)), FAKE, FAKE, FAKE,
+                                   table, lens, 8, FAKE, FAKE, 4, FAKE, 1 << 40, None,
+                                   None) == m.MALA_ERR_INVALID_ARG
