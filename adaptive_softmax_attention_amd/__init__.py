@@ -279,7 +279,7 @@ def fullattn_decode(q, k_cache, v_cache, o, lse, num_splits, workspace, *, block
 
 
 def _decode_paged(name, q, k_pages, v_pages, block_table, cache_lens, max_len, o, lse,
-                  num_splits, workspace, tau, softmax_scale, stats, stream):
+                  num_splits, workspace, tau, block_k, softmax_scale, stats, stream):
     import torch
     B, Hq, d = q.shape
     P, Hkv = k_pages.shape[0], k_pages.shape[1]
@@ -293,7 +293,7 @@ def _decode_paged(name, q, k_pages, v_pages, block_table, cache_lens, max_len, o
     if workspace is None or not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace: a contiguous device tensor is required")
     shp = Shape(B, Hq, Hkv, 1, int(max_len), d)
-    cfg = make_config(False, tau, 64, 64, softmax_scale, d)
+    cfg = make_config(False, tau, 64, block_k, softmax_scale, d)
     st = stats._c() if stats is not None else None
     nbytes = workspace.numel() * workspace.element_size()
     rc = getattr(lib(), name)(ctypes.byref(shp), ctypes.byref(cfg), _ptr(q), _ptr(k_pages),
@@ -311,17 +311,19 @@ def mala_decode_paged_workspace_bytes(q, max_len, heads_kv, num_splits):
 
 
 def mala_decode_paged(q, k_pages, v_pages, block_table, cache_lens, max_len, o, lse, num_splits,
-                      workspace, *, tau=1.0, softmax_scale=None, stats=None, stream=None):
+                      workspace, *, tau=1.0, block_k=64, softmax_scale=None, stats=None,
+                      stream=None):
     """Split-KV MALA decode over a paged cache of variable-length sequences:
     q/o [B,Hq,d] bf16, lse [B,Hq] fp32, pages [P,Hkv,64,d] bf16, block_table
     [B, ceil(max_len/64)] int32, cache_lens [B] int32 (1..max_len), all on the
-    device."""
+    device. block_k (64 or 128) is the decision tile; pages stay 64 keys."""
     _decode_paged("mala_decode_paged", q, k_pages, v_pages, block_table, cache_lens, max_len, o,
-                  lse, num_splits, workspace, tau, softmax_scale, stats, stream)
+                  lse, num_splits, workspace, tau, block_k, softmax_scale, stats, stream)
 
 
 def fullattn_decode_paged(q, k_pages, v_pages, block_table, cache_lens, max_len, o, lse,
-                          num_splits, workspace, *, softmax_scale=None, stats=None, stream=None):
+                          num_splits, workspace, *, block_k=64, softmax_scale=None, stats=None,
+                          stream=None):
     """Dense split-KV decode over the same paged cache."""
     _decode_paged("fullattn_decode_paged", q, k_pages, v_pages, block_table, cache_lens, max_len,
-                  o, lse, num_splits, workspace, 0.0, softmax_scale, stats, stream)
+                  o, lse, num_splits, workspace, 0.0, block_k, softmax_scale, stats, stream)

@@ -39,7 +39,8 @@ int check_config(const mala_config* c, bool uses_tau) {
   if (!c) return MALA_ERR_INVALID_ARG;
   if (c->causal != 0 && c->causal != 1) return MALA_ERR_INVALID_ARG;
   if (c->block_q < 1 || c->block_k < 1) return MALA_ERR_INVALID_ARG;
-  if (c->block_q != 64 || c->block_k != 64) return MALA_ERR_UNSUPPORTED;
+  if ((c->block_q != 64 && c->block_q != 128) || (c->block_k != 64 && c->block_k != 128))
+    return MALA_ERR_UNSUPPORTED;
   if (!(c->softmax_scale > 0.f) || isinf(c->softmax_scale)) return MALA_ERR_INVALID_ARG;
   if (uses_tau && (isnan(c->tau) || c->tau < 0.f)) return MALA_ERR_INVALID_ARG;
   return MALA_OK;
@@ -107,6 +108,8 @@ int fwd_common(const mala_shape* shape, const mala_config* cfg, const void* q, c
   a.nk = shape->seqlen_k;
   a.head_dim = shape->head_dim;
   a.causal = cfg->causal;
+  a.block_q = cfg->block_q;
+  a.block_k = cfg->block_k;
   a.scale = cfg->softmax_scale;
   a.tau = test ? cfg->tau : 0.f;
   a.counters = stats ? stats->counters : nullptr;
@@ -163,6 +166,8 @@ int bwd_common(const mala_shape* shape, const mala_config* cfg, const void* q, c
   a.nk = shape->seqlen_k;
   a.head_dim = shape->head_dim;
   a.causal = cfg->causal;
+  a.block_q = cfg->block_q;
+  a.block_k = cfg->block_k;
   a.scale = cfg->softmax_scale;
   a.tau = test ? cfg->tau : 0.f;
   a.counters = stats ? stats->counters : nullptr;
@@ -188,8 +193,8 @@ int decode_common(const mala_shape* shape, const mala_config* cfg, const void* q
     return MALA_ERR_INVALID_ARG;
   if (shape->heads_q / shape->heads_kv > 8) return MALA_ERR_UNSUPPORTED;
   if (num_splits < 1) return MALA_ERR_INVALID_ARG;
-  const int64_t tc = (shape->seqlen_k + 63) / 64;
-  if (num_splits > tc) return MALA_ERR_INVALID_ARG;  // every split owns >= 1 tile
+  const int64_t tc = (shape->seqlen_k + cfg->block_k - 1) / cfg->block_k;
+  if (num_splits > tc) return MALA_ERR_INVALID_ARG;  // every split owns >= 1 decision tile
   const size_t need = mala_decode_workspace_bytes(shape, num_splits);
   if (!workspace || workspace_bytes < need) return MALA_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return MALA_ERR_INVALID_ARG;
@@ -212,6 +217,7 @@ int decode_common(const mala_shape* shape, const mala_config* cfg, const void* q
   a.nk = shape->seqlen_k;
   a.head_dim = shape->head_dim;
   a.num_splits = num_splits;
+  a.block_k = cfg->block_k;
   a.scale = cfg->softmax_scale;
   a.tau = test ? cfg->tau : 0.f;
   a.counters = stats ? stats->counters : nullptr;

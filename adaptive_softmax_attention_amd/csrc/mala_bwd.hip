@@ -79,6 +79,7 @@ struct BwdParams {
   int* work;    // [B*Hkv][wmax] dK/dV work items: pair | seg << 20 | nseg << 24
   int* wcnt;    // [B*Hkv] work items per (batch, KV head)
   int wmax;     // work item slots per (batch, KV head)
+  int kq, kk;   // 64-row / 64-key sub-tiles per decision tile (block_q / 64, block_k / 64)
   unsigned long long* counters;
   uint8_t* decisions;
 };
@@ -391,6 +392,70 @@ __global__ __launch_bounds__(576, 1) void bwd_score_kernel(BwdParams p) {
   // kept items per key block (waves x and x + 4 score block x)
   if (tid < NB && jb0 + tid < p.tc)
     p.kcount[(size_t)bk * p.tc + jb0 + tid] = csum[tid] + csum[tid + 4];
+}
+
+// ----------------------------------------------------------- coarsen ----
+// Decision tiles of block_q x block_k = (64 kq) x (64 kk) (kq, kk in {1, 2}).
+// The offline test of Eq. 4 keeps a tile iff some legal entry passes, so a
+// coarse tile is kept iff one of its legal 64 x 64 sub-tiles is: the scoring
+// pass decides the sub-tiles, and this pass ORs them and writes the result
+// back into every legal sub-tile, so the dK/dV and dQ passes read the map as
+// usual. One workgroup per (batch, KV head, coarse key column) walks the
+// column's (query head, coarse query block) items; it also recounts the kept
+// items of each 64-key block for the pairing pass and, when instrumented,
+// counts and records the decisions per coarse tile.
+template <bool kStats>
+__global__ __launch_bounds__(256) void bwd_coarsen_kernel(BwdParams p) {
+  __shared__ int cnt[2];
+  __shared__ unsigned long long st[3];
+  const int per = p.batch * p.heads_kv;
+  const int bk = (int)(blockIdx.x % per), jc = (int)(blockIdx.x / per);
+  const int b = bk / p.heads_kv, kvh = bk % p.heads_kv;
+  const int trc = (p.tr + p.kq - 1) / p.kq, tcc = (p.tc + p.kk - 1) / p.kk;
+  const int j0 = p.kk * jc, j1 = min(p.tc, j0 + p.kk);
+  if (threadIdx.x < 2) cnt[threadIdx.x] = 0;
+  if (threadIdx.x < 3) st[threadIdx.x] = 0;
+  __syncthreads();
+  int mycnt[2] = {0, 0};
+  unsigned long long s_legal = 0, s_kept = 0, s_slots = 0;
+  const int n_items = p.group * trc;
+  for (int t = threadIdx.x; t < n_items; t += 256) {
+    const int h = kvh * p.group + t % p.group, ic = t / p.group;
+    const int bh = b * p.heads_q + h;
+    const int i0 = p.kq * ic, i1 = min(p.tr, i0 + p.kq);
+    bool any_legal = false, keep = false;
+    for (int i = i0; i < i1; ++i)
+      for (int j = j0; j < j1; ++j)
+        if (reaches(p, i, j)) {
+          any_legal = true;
+          keep = keep || p.dmap[dmap_index(p, bh, i, j)] != 0;
+        }
+    if (!any_legal) continue;
+    for (int i = i0; i < i1; ++i)
+      for (int j = j0; j < j1; ++j)
+        if (reaches(p, i, j)) {
+          p.dmap[dmap_index(p, bh, i, j)] = keep ? 1 : 0;
+          if (keep) ++mycnt[j - j0];
+        }
+    if (kStats) {
+      ++s_legal;
+      if (keep) {
+        ++s_kept;
+        s_slots += (unsigned long long)(min(p.nq, 64 * i1) - 64 * i0) * (64ull * p.kk);
+      }
+      if (p.decisions) p.decisions[((size_t)bh * trc + ic) * tcc + jc] = keep ? 1 : 0;
+    }
+  }
+  atomicAdd(&cnt[0], mycnt[0]);
+  atomicAdd(&cnt[1], mycnt[1]);
+  if (kStats) {
+    atomicAdd(&st[0], s_legal);
+    atomicAdd(&st[1], s_kept);
+    atomicAdd(&st[2], s_slots);
+  }
+  __syncthreads();
+  if (threadIdx.x < j1 - j0) p.kcount[(size_t)bk * p.tc + j0 + threadIdx.x] = cnt[threadIdx.x];
+  if (kStats && threadIdx.x < 3 && p.counters) atomicAdd(&p.counters[threadIdx.x], st[threadIdx.x]);
 }
 
 // Dense path without instrumentation: every legal tile is kept, so the
@@ -1076,7 +1141,12 @@ hipError_t launch_all(const BwdParams& p, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long per = (long long)p.batch * p.heads_kv;
-  if (kTest || kStats) {
+  const bool coarse = p.kq * p.kk > 1;
+  if (kTest && coarse) {
+    // 64 x 64 sub-tile decisions; counting and recording happen per coarse tile
+    hipLaunchKernelGGL((bwd_score_kernel<D, true, false>),
+                       dim3((unsigned)(((p.tc + 3) / 4) * per)), dim3(576), 0, stream, p);
+  } else if (kTest || (kStats && !coarse)) {
     hipLaunchKernelGGL((bwd_score_kernel<D, kTest, kStats>),
                        dim3((unsigned)(((p.tc + 3) / 4) * per)), dim3(576), 0, stream, p);
   } else {
@@ -1086,6 +1156,13 @@ hipError_t launch_all(const BwdParams& p, hipStream_t stream) {
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (coarse && (kTest || kStats)) {
+    const long long tcc = (p.tc + p.kk - 1) / p.kk;
+    hipLaunchKernelGGL((bwd_coarsen_kernel<kStats>), dim3((unsigned)(tcc * per)), dim3(256), 0,
+                       stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   BwdParams q = p;
   if (kTest) {
     hipLaunchKernelGGL(bwd_pair_kernel, dim3((unsigned)per), dim3(256), 0, stream, p);
@@ -1188,6 +1265,8 @@ hipError_t launch_bwd(const BwdArgs& a, bool test, hipStream_t stream) {
   }
   p.n_hg = p.group / p.hpw;
   p.n_ig = (p.tr + p.ipw - 1) / p.ipw;
+  p.kq = a.block_q / 64;
+  p.kk = a.block_k / 64;
   p.counters = a.counters;
   p.decisions = a.decisions;
   return a.head_dim == 128 ? launch_d<128>(p, test, stream) : launch_d<64>(p, test, stream);

@@ -38,6 +38,8 @@ struct DecParams {
   float* part_l;
   float* part_u;
   int batch, heads_q, heads_kv, nk, group, splits, per, tc;
+  int kk;   // 64-key tiles per decision tile (block_k / 64)
+  int tcd;  // decision tiles of the longest cache (row length of the decision bitmap)
   float c;         // softmax_scale * log2(e)
   float thr;       // log2(tau / nk)
   float log2_tau;  // log2(tau); -inf for tau = 0
@@ -52,7 +54,7 @@ struct DecParams {
   uint8_t* decisions;
 };
 
-template <int D, int GM, bool kTest, bool kStats>
+template <int D, int GM, bool kTest, bool kStats, bool kBK2>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecParams p) {
   constexpr int NDC = D / 32;   // reduction chunks of d for the score MFMA
   constexpr int DG = D / 8;     // 8-column groups of d (P V lanes)
@@ -79,7 +81,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecParams p) {
     bad = nk < 1 || nk > p.nk;
     nk = bad ? 0 : nk;
     tc = (nk + 63) / 64;
-    per = (tc + p.splits - 1) / p.splits;
+    // splits cut the sequence's own decision tiles
+    per = p.kk * (((tc + p.kk - 1) / p.kk + p.splits - 1) / p.splits);
     thr = p.log2_tau - log2f((float)max(nk, 1));
   }
   const int j_lo = s * per;
@@ -124,16 +127,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecParams p) {
     };
     load_k(j_hi);
     unsigned long long st_legal = 0, st_kept = 0, st_vtiles = 0;  // instrumentation
-    for (int j = j_hi; j >= j_lo; --j) {
-      floatx4 sc[4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        sc[ks] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int dc = 0; dc < NDC; ++dc) sc[ks] = mfma16x16x32(kr[ks][dc], qb[dc], sc[ks]);
-      }
-      if (j > j_lo) load_k(j - 1);  // next tile streams while this one is tested
-      // lane holds keys 16ks + 4g4 + r of head column l16
+    // this head's maximum over a scored tile (raw units), keys past the end masked
+    auto tile_max = [&](floatx4 (&sc)[4], int j) {
       float mt = -INFINITY;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
@@ -143,25 +138,19 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecParams p) {
           if (key >= nk) sc[ks][r] = -INFINITY;
           mt = fmaxf(mt, sc[ks][r]);
         }
-      mt = group4_max(mt);
-      bool want;
-      if constexpr (kTest) {
-        // Eq. 3 for this head's single row, against the split's own (m, l)
-        want = col_ok && (lsum == 0.f || !(mt * p.c - m2 - fast_log2(lsum) - thr < 0.f));
-      } else {
-        want = col_ok;
-      }
-      if (col_ok && g4 == 0) {
-        if (kStats) {
-          ++st_legal;
-          if (want) ++st_kept;
-        }
-        if (kStats && p.decisions)
-          p.decisions[(size_t)(b * p.heads_q + h0 + l16) * p.tc + j] = want ? 1 : 0;
-      }
-      if (!wave_any(want)) continue;  // no head retains: V tile never read
+      return group4_max(mt);
+    };
+    // Eq. 3 for this head's single row, against the split's own (m, l)
+    auto vote = [&](float mt) {
+      if constexpr (kTest)
+        return col_ok && (lsum == 0.f || !(mt * p.c - m2 - fast_log2(lsum) - thr < 0.f));
+      else
+        return col_ok;
+    };
+    // read V of tile j (some head retains it), update the retaining heads'
+    // (m, l) and add P V for them
+    auto apply = [&](floatx4 (&sc)[4], float mt, bool want, int j) {
       if (kStats) ++st_vtiles;
-
       bf16x8 vr[KT];
       const __bf16* vt = tile_k(p.v, j);
 #pragma unroll
@@ -221,6 +210,68 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecParams p) {
         }
       }
       lds_barrier();
+    };
+    // 128-key decision tiles are the pairs (2 jc + 1, 2 jc) of 64-key tiles,
+    // visited upper first. A head that retains the upper tile under the
+    // pair's state has retained the pair; a head whose vote passes only on
+    // the lower tile (its state unchanged by the upper one) retains the pair
+    // late: the upper tile is scored again from memory and applied after the
+    // lower one (the online update is independent of the order).
+    bool early = false;
+    for (int j = j_hi; j >= j_lo; --j) {
+      floatx4 sc[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        sc[ks] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dc = 0; dc < NDC; ++dc) sc[ks] = mfma16x16x32(kr[ks][dc], qb[dc], sc[ks]);
+      }
+      if (j > j_lo) load_k(j - 1);  // next tile streams while this one is tested
+      // lane holds keys 16ks + 4g4 + r of head column l16
+      const float mt = tile_max(sc, j);
+      const bool v = vote(mt);
+      bool want = v, late = false, record = true;
+      if constexpr (kBK2) {
+        if (j & 1) {  // upper tile: decided with the lower one
+          want = v;
+          early = v;
+          record = false;
+        } else {
+          want = early || v;
+          late = !early && v && j + 1 <= j_hi;
+          early = false;
+        }
+      }
+      if (record && col_ok && g4 == 0) {
+        if (kStats) {
+          ++st_legal;
+          if (want) ++st_kept;
+        }
+        if (kStats && p.decisions)
+          p.decisions[(size_t)(b * p.heads_q + h0 + l16) * p.tcd + (kBK2 ? j / 2 : j)] = want ? 1 : 0;
+      }
+      if (wave_any(want)) apply(sc, mt, want, j);  // else no head retains: V never read
+      if constexpr (kBK2) {
+        if (wave_any(late)) {
+          // score the upper tile again (its K straight from memory)
+          const int jh = j + 1;
+          const __bf16* kt = tile_k(p.k, jh);
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            sc[ks] = floatx4{0.f, 0.f, 0.f, 0.f};
+            const int key = jh * 64 + 16 * ks + l16;
+#pragma unroll
+            for (int dc = 0; dc < NDC; ++dc) {
+              const bf16x8 kk = (kt && key < nk)
+                                    ? *(const bf16x8*)(kt + (size_t)(16 * ks + l16) * D + 32 * dc + 8 * g4)
+                                    : bf16x8{};
+              sc[ks] = mfma16x16x32(kk, qb[dc], sc[ks]);
+            }
+          }
+          const float mh = tile_max(sc, jh);
+          apply(sc, mh, late, jh);
+        }
+      }
     }
     if (kStats && p.counters) {
 #pragma unroll
@@ -231,7 +282,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecParams p) {
       if (lane == 0) {
         atomicAdd(&p.counters[0], st_legal);
         atomicAdd(&p.counters[1], st_kept);
-        atomicAdd(&p.counters[2], 64ull * st_kept);
+        atomicAdd(&p.counters[2], 64ull * p.kk * st_kept);
         atomicAdd(&p.counters[3], st_vtiles);
       }
     }
@@ -291,14 +342,23 @@ template <int D, int GM>
 hipError_t launch_d(const DecParams& p, bool test, hipStream_t stream) {
   dim3 grid((unsigned)(p.batch * p.heads_kv * p.splits)), block(64);
   const bool st = p.counters != nullptr || p.decisions != nullptr;
-  if (test && st)
-    hipLaunchKernelGGL((decode_split_kernel<D, GM, true, true>), grid, block, 0, stream, p);
+  // 128-key decisions matter to the test and to the recorded decisions; the
+  // dense path without instrumentation computes the same either way
+  const bool bk2 = p.kk == 2;
+  if (test && st && bk2)
+    hipLaunchKernelGGL((decode_split_kernel<D, GM, true, true, true>), grid, block, 0, stream, p);
+  else if (test && st)
+    hipLaunchKernelGGL((decode_split_kernel<D, GM, true, true, false>), grid, block, 0, stream, p);
+  else if (test && bk2)
+    hipLaunchKernelGGL((decode_split_kernel<D, GM, true, false, true>), grid, block, 0, stream, p);
   else if (test)
-    hipLaunchKernelGGL((decode_split_kernel<D, GM, true, false>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_split_kernel<D, GM, true, false, false>), grid, block, 0, stream, p);
+  else if (st && bk2)
+    hipLaunchKernelGGL((decode_split_kernel<D, GM, false, true, true>), grid, block, 0, stream, p);
   else if (st)
-    hipLaunchKernelGGL((decode_split_kernel<D, GM, false, true>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_split_kernel<D, GM, false, true, false>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((decode_split_kernel<D, GM, false, false>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_split_kernel<D, GM, false, false, false>), grid, block, 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(p.batch * p.heads_q), dim3(D), 0, stream, p);
@@ -332,7 +392,10 @@ hipError_t launch_decode(const DecodeArgs& a, bool test, hipStream_t stream) {
   p.group = a.heads_q / a.heads_kv;
   p.splits = a.num_splits;
   p.tc = (a.nk + 63) / 64;
-  p.per = (p.tc + a.num_splits - 1) / a.num_splits;
+  p.kk = a.block_k / 64;
+  p.tcd = (a.nk + a.block_k - 1) / a.block_k;
+  // splits cut the decision tiles: ceil(tcd / S) of them, in 64-key tiles
+  p.per = p.kk * ((p.tcd + a.num_splits - 1) / a.num_splits);
   p.c = a.scale * kLog2e;
   const float log2_tau = a.tau == 0.f ? -INFINITY : log2f(a.tau);
   p.thr = log2_tau - log2f((float)a.nk);

@@ -50,18 +50,23 @@ struct FwdParams {
   int hpw, ipw;    // heads x query blocks per workgroup, hpw * ipw = 4
   int n_hg, n_ig;  // head groups per KV head, query-block groups
   int tr, tc;      // query / key tile counts
+  int trd, tcd;    // decision tiles (block_q x block_k) along queries / keys
   unsigned long long* counters;
   uint8_t* decisions;
 };
 
-template <int D, bool kTest, bool kStats>
+// kBQ2 / kBK2: decision tiles of 128 rows / 128 keys (pairs of the 64 x 64
+// compute tiles); both false is the 64 x 64 tile.
+template <int D, bool kTest, bool kStats, bool kBQ2, bool kBK2>
 __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   constexpr int NDC = D / 16;         // 16-wide reduction chunks over d
   constexpr int NDT = D / 32;         // 32-row subtiles of O^T over d
   constexpr int KCH = D / 8;          // 16-byte chunks per K / V row
   constexpr int NT = 512;             // threads per workgroup (8 waves)
   constexpr int CPT = 64 * KCH / NT;  // async 16-byte copies per thread per tile
-  constexpr int RK = 3;               // K ring: current tile + 2 ahead
+  // K ring: current tile + 2 ahead (+ the previous one, whose scores a late
+  // 128-key decision forms again)
+  constexpr int RK = kBK2 ? 4 : 3;
   constexpr int RV = 2;               // V ring
   constexpr uint32_t kTileBytes = 64 * D * 2;
   // The exponentials are taken against a reference maximum that moves only
@@ -73,6 +78,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) __bf16 v_ring[RV][64 * D];
   __shared__ int vflags[2][8];  // block decisions, read after the next barrier
   __shared__ int pflags[8];     // row-half ballots, tagged with the tile
+  __shared__ int lflags[8];     // 128-key tiles: V of the upper tile requested late
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
@@ -97,6 +103,18 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   const int i_top = min(ig * p.ipw + p.ipw - 1, p.tr - 1);
   const int jtop = p.causal ? min(p.tc - 1, i_top + p.cblk) : p.tc - 1;
   const int vrows = valid ? min(64, p.nq - i * 64) : 0;
+  // 128-row decision tiles: the block is paired with query block i ^ 1 of
+  // the same head (block pblk of the group, hpw in {1, 2}); the four waves
+  // of the pair decide together, over the key tiles either block reaches
+  const int pblk = blk ^ p.hpw;
+  const int pi = i ^ 1;
+  const bool pvalid = kBQ2 && pi < p.tr;
+  const int pjmax = pvalid ? (p.causal ? min(p.tc - 1, pi + p.cblk) : p.tc - 1) : -1;
+  const int jmax_x = kBQ2 ? max(jmax, pjmax) : jmax;
+  const int prows = pvalid ? min(64, p.nq - pi * 64) : 0;
+  // the wave that records a decision tile's outcome: the upper block of a
+  // 128-row pair (or the lower one when the upper lies past the end)
+  const bool recorder = kBQ2 ? ((i & 1) ? valid : (valid && !pvalid)) : valid;
 
   const size_t qrow0 = (size_t)(b * p.heads_q + h) * p.nq;
   const __bf16* kbase = p.k + (size_t)(b * p.heads_kv + kvh) * p.nk * D;
@@ -218,6 +236,27 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
       pb[kc] = t;
     }
   };
+  // the exponentials of a tile against a given reference and its bf16 P
+  // operand (as above); returns this lane's part of the row sum
+  auto exp_pack = [&](floatx16 (&s)[2], float mu, bf16x8 (&pb)[4]) {
+    float rs = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float pv = fast_exp2(s[kt][e] * p.c - mu);
+        s[kt][e] = pv;
+        rs += pv;
+      }
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      bf16x8 t;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t[e] = to_bf16(s[kc >> 1][8 * (kc & 1) + e]);
+      pb[kc] = t;
+    }
+    return rs;
+  };
   // O^T += V^T P^T over one tile; the V^T operand of key chunk kc holds keys
   // 16kc + 4hh + 0..3 and 16kc + 8 + 4hh + 0..3 of column 32dt + l32
   const int g16 = lane >> 4, j16 = lane & 15;
@@ -253,12 +292,48 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   float mt = -INFINITY, alA = 1.f, alB = 1.f;
   bool pendA = false, pendB = false;  // P V outstanding for the tile in that set
   bool d_last = false;                // this block's decision on tile j+1
+  // 128-key decision tiles are the pairs (2 J + 1, 2 J) of key tiles, upper
+  // first: the upper tile's group decision, this block's row maximum on it
+  // and whether this block has legal keys in it
+  bool early = false, s_hi = false;
+  float mt_hi = -INFINITY;
   unsigned long long st_legal = 0, st_kept = 0, st_slots = 0, st_vtiles = 0;  // instrumentation
 
   issue_tile(kbase, jtop, k_lds + (jtop % RK) * kTileBytes, false);
   if (jtop >= 1) issue_tile(kbase, jtop - 1, k_lds + ((jtop - 1) % RK) * kTileBytes, false);
 
-  auto step = [&](int j, bf16x8 (&pset)[4], float& al, bool& pend) {
+  // publish this wave's vote on tile j tagged with the tile, then OR in the
+  // votes of the waves that decide the tile with it: the other row half of
+  // the block and, with 128-row tiles, both halves of the paired block. All
+  // of them take this path for the same tiles and nothing between the
+  // barrier and here waits on another wave, so the waits end.
+  auto exchange = [&](int j, bool mine) {
+    const int tag = 2 * (j + 1);
+    __hip_atomic_store(&pflags[w], tag | (mine ? 1 : 0), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_WORKGROUP);
+    bool any = mine;
+    auto take = [&](int x) {
+      int o;
+      do {
+        o = __hip_atomic_load(&pflags[x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      } while ((o & ~1) != tag);
+      any = any || (o & 1);
+    };
+    take(w ^ 1);
+    if constexpr (kBQ2) {
+      take(2 * pblk);
+      take(2 * pblk + 1);
+    }
+    return any;
+  };
+  const auto needs_mask = [&](int t) {
+    return (p.causal && t * 64 + 63 > i * 64 + p.off) || (t * 64 + 63 >= p.nk);
+  };
+
+  // pset / al / pend: the register set of tiles j, j + 2; poth / aloth /
+  // pendoth: the other set (tiles j + 1, j - 1)
+  auto step = [&](int j, bf16x8 (&pset)[4], float& al, bool& pend, bf16x8 (&poth)[4],
+                  float& aloth, bool& pendoth) {
     // K_j and V_{j+2} complete (K_{j-1} may stay in flight); decisions on
     // tile j+1 published
     vmcnt_wait_le(j >= 1 ? CPT : 0);
@@ -269,14 +344,16 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
       const int* f = vflags[jn & 1];
 #pragma unroll
       for (int x = 0; x < 8; ++x) any1 |= f[x];
-      if (kStats && valid && jn <= jmax && half == 0 && lane == 0) {
-        ++st_legal;
-        if (d_last) {
-          ++st_kept;
-          st_slots += (unsigned long long)vrows * 64ull;
+      if constexpr (!(kBQ2 || kBK2)) {
+        if (kStats && valid && jn <= jmax && half == 0 && lane == 0) {
+          ++st_legal;
+          if (d_last) {
+            ++st_kept;
+            st_slots += (unsigned long long)vrows * 64ull;
+          }
+          if (p.decisions)
+            p.decisions[((size_t)(b * p.heads_q + h) * p.tr + i) * p.tc + jn] = d_last ? 1 : 0;
         }
-        if (p.decisions)
-          p.decisions[((size_t)(b * p.heads_q + h) * p.tr + i) * p.tc + jn] = d_last ? 1 : 0;
       }
     }
     // V of tile j+1 only if some block retains it; then K two tiles ahead
@@ -284,35 +361,83 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
       issue_tile(vbase, jn, v_lds + (jn % RV) * kTileBytes, true);
       if (kStats) ++st_vtiles;
     }
+    int anyl = 0;
+    if constexpr (kBK2) {
+      // an upper tile j+2 kept late (decided at iteration j+1, a lower
+      // tile): its V now, and it must land before its P V below
+      if (jn >= 0 && jn <= jtop && !(jn & 1)) {
+#pragma unroll
+        for (int x = 0; x < 8; ++x) anyl |= lflags[x];
+      }
+      if (anyl) {
+        issue_tile(vbase, j + 2, v_lds + ((j + 2) % RV) * kTileBytes, true);
+        if (kStats) ++st_vtiles;
+      }
+    }
     if (j >= 2) issue_tile(kbase, j - 2, k_lds + ((j - 2) % RK) * kTileBytes, false);
+    if constexpr (kBK2) {
+      if (anyl) {  // the same for every wave: anyl is read after the barrier
+        vmcnt_wait_le(j >= 2 ? CPT : 0);
+        lds_barrier();
+      }
+    }
 
     // scores and decision of tile j
     const bool do_s = j >= 0 && valid && j <= jmax;
-    bool dj = false;
+    const bool do_x = kBQ2 ? (j >= 0 && j <= jmax_x) : do_s;  // this wave's group decides tile j
+    bool dj = false;    // the group keeps tile j
+    bool late = false;  // 128 keys, lower tile: the group keeps the pair only now
     if (do_s) {
       score(&k_ring[0][0] + (j % RK) * 64 * D, sc);
-      if ((p.causal && j * 64 + 63 > i * 64 + p.off) || (j * 64 + 63 >= p.nk)) mask(sc, j);
-      const bool mine = vote(sc, mt);
-      if constexpr (kTest) {
-        // publish this half's vote tagged with the tile, then wait for the
-        // other half's vote on the same tile. Both halves take this path
-        // for the same tiles and nothing between the barrier and here
-        // waits on another wave, so the wait ends.
-        const int tag = 2 * (j + 1);
-        __hip_atomic_store(&pflags[w], tag | (mine ? 1 : 0), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_WORKGROUP);
-        int other;
-        do {
-          other = __hip_atomic_load(&pflags[w ^ 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        } while ((other & ~1) != tag);
-        dj = mine || (other & 1);
+      if (needs_mask(j)) mask(sc, j);
+    }
+    if (do_x) {
+      bool mine = false;
+      if (do_s) {
+        mine = vote(sc, mt);
       } else {
-        dj = true;
+        mt = -INFINITY;
+      }
+      bool v = true;
+      if constexpr (kTest) v = exchange(j, mine);
+      if constexpr (kBK2) {
+        if (j & 1) {  // upper tile: the pair is kept now iff it passes here
+          early = v;
+          dj = v;
+          mt_hi = mt;
+          s_hi = do_s;
+        } else {  // lower tile, tested against the same state unless kept early
+          dj = early || v;
+          late = !early && v && s_hi;
+        }
+      } else {
+        dj = v;
       }
     }
+    const bool own = dj && do_s;  // this block's rows take tile j's update
     // every lane stores the same word: no divergent branch needed
-    if (j >= 0) vflags[j & 1][w] = dj ? 1 : 0;
-    d_last = dj;
+    if (j >= 0) vflags[j & 1][w] = own ? 1 : 0;
+    d_last = own;
+    if constexpr (kBK2) {
+      if (j >= 0 && !(j & 1)) {
+        lflags[w] = late ? 1 : 0;
+        early = false;
+        s_hi = false;
+      }
+    }
+    if constexpr (kStats && (kBQ2 || kBK2)) {
+      // one wave records each decision tile (of a pair, on its lower tile)
+      if (do_x && recorder && half == 0 && lane == 0 && (!kBK2 || !(j & 1))) {
+        ++st_legal;
+        if (dj) {
+          ++st_kept;
+          st_slots += (unsigned long long)(vrows + prows) * (kBK2 ? 128ull : 64ull);
+        }
+        if (p.decisions)
+          p.decisions[((size_t)(b * p.heads_q + h) * p.trd + (kBQ2 ? i / 2 : i)) * p.tcd +
+                      (kBK2 ? j / 2 : j)] = dj ? 1 : 0;
+      }
+    }
 
     // P V of tile j+2 with the softmax of tile j
     const bool pv_old = pend;
@@ -324,21 +449,46 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
         for (int e = 0; e < 16; ++e) oacc[dt][e] *= al;
     }
     const __bf16* vt = &v_ring[0][0] + ((j + 2) % RV) * 64 * D;
-    if (pv_old && dj) {
+    if constexpr (kBK2) {
+      if (late && do_s) {
+        // the pair is kept late: one reference maximum for both tiles, the
+        // lower tile's P from its scores, the upper tile's scores formed
+        // again from its K (still in the ring); the upper tile's P V comes
+        // first and carries the rescale
+        if (pv_old) pv(vt, pset);
+        const float mtc = fmaxf(mt, mt_hi) * p.c;
+        const bool mv = mtc > mref + kLazy;
+        const float mnew = mv ? mtc : mref;
+        const float mu = (mnew == -INFINITY) ? 0.f : mnew;
+        const float alpha = mv ? fast_exp2(mref - mu) : 1.f;
+        mref = mnew;
+        float rs = exp_pack(sc, mu, pset);
+        score(&k_ring[0][0] + ((j + 1) % RK) * 64 * D, sc);
+        if (needs_mask(j + 1)) mask(sc, j + 1);
+        rs += exp_pack(sc, mu, poth);
+        lsum = alpha * lsum + pair32_sum(rs);
+        aloth = alpha;
+        al = 1.f;
+        pendoth = true;
+        pend = true;
+        return;
+      }
+    }
+    if (pv_old && own) {
       pv(vt, pset);
       softmax(sc, mt, al, pset);
     } else if (pv_old) {
       pv(vt, pset);
-    } else if (dj) {
+    } else if (own) {
       softmax(sc, mt, al, pset);
     }
-    pend = dj;
+    pend = own;
   };
 
   // j runs down to -2 to drain the pipeline
   for (int j = jtop; j >= -2; j -= 2) {
-    step(j, pA, alA, pendA);
-    if (j - 1 >= -2) step(j - 1, pB, alB, pendB);
+    step(j, pA, alA, pendA, pB, alB, pendB);
+    if (j - 1 >= -2) step(j - 1, pB, alB, pendB, pA, alA, pendA);
   }
 
   if (kStats && p.counters && lane == 0) {
@@ -368,6 +518,28 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
 
 }  // namespace
 
+template <int D, bool kTest, bool kStats>
+hipError_t launch_ft(const FwdParams& p, int mode, dim3 grid, dim3 block, hipStream_t stream) {
+  switch (mode) {
+    case 0: hipLaunchKernelGGL((fwd_kernel<D, kTest, kStats, false, false>), grid, block, 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((fwd_kernel<D, kTest, kStats, false, true>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((fwd_kernel<D, kTest, kStats, true, false>), grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL((fwd_kernel<D, kTest, kStats, true, true>), grid, block, 0, stream, p); break;
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_fm(const FwdParams& p, bool test, bool st, int mode, dim3 grid, dim3 block,
+                     hipStream_t stream) {
+  if (test && st) return launch_ft<D, true, true>(p, mode, grid, block, stream);
+  if (test) return launch_ft<D, true, false>(p, mode, grid, block, stream);
+  if (st) return launch_ft<D, false, true>(p, mode, grid, block, stream);
+  // dense and not instrumented: the decision tile changes nothing
+  hipLaunchKernelGGL((fwd_kernel<D, false, false, false, false>), grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_fwd(const FwdArgs& a, bool test, hipStream_t stream) {
   FwdParams p;
   p.q = (const __bf16*)a.q;
@@ -386,7 +558,8 @@ hipError_t launch_fwd(const FwdArgs& a, bool test, hipStream_t stream) {
   p.c = a.scale * kLog2e;
   p.log2_tau = a.tau == 0.f ? -INFINITY : log2f(a.tau);
   p.group = a.heads_q / a.heads_kv;
-  if (p.group % 4 == 0) {
+  const bool bq2 = a.block_q == 128, bk2 = a.block_k == 128;
+  if (p.group % 4 == 0 && !bq2) {
     p.hpw = 4;
     p.ipw = 1;
   } else if (p.group % 2 == 0) {
@@ -398,6 +571,8 @@ hipError_t launch_fwd(const FwdArgs& a, bool test, hipStream_t stream) {
   }
   p.tr = (a.nq + 63) / 64;
   p.tc = (a.nk + 63) / 64;
+  p.trd = (a.nq + a.block_q - 1) / a.block_q;
+  p.tcd = (a.nk + a.block_k - 1) / a.block_k;
   p.n_hg = p.group / p.hpw;
   p.n_ig = (p.tr + p.ipw - 1) / p.ipw;
   p.counters = a.counters;
@@ -405,28 +580,12 @@ hipError_t launch_fwd(const FwdArgs& a, bool test, hipStream_t stream) {
   const long long nblocks = (long long)p.n_ig * p.batch * p.heads_kv * p.n_hg;
   dim3 grid((unsigned)nblocks), block(512);
   // the instrumented variant is a separate instantiation, so the timed
-  // kernel carries no counter code
+  // kernel carries no counter code; the decision tile matters to the test
+  // and to what the instrumentation records
   const bool st = p.counters != nullptr || p.decisions != nullptr;
-  if (a.head_dim == 128) {
-    if (test && st)
-      hipLaunchKernelGGL((fwd_kernel<128, true, true>), grid, block, 0, stream, p);
-    else if (test)
-      hipLaunchKernelGGL((fwd_kernel<128, true, false>), grid, block, 0, stream, p);
-    else if (st)
-      hipLaunchKernelGGL((fwd_kernel<128, false, true>), grid, block, 0, stream, p);
-    else
-      hipLaunchKernelGGL((fwd_kernel<128, false, false>), grid, block, 0, stream, p);
-  } else {
-    if (test && st)
-      hipLaunchKernelGGL((fwd_kernel<64, true, true>), grid, block, 0, stream, p);
-    else if (test)
-      hipLaunchKernelGGL((fwd_kernel<64, true, false>), grid, block, 0, stream, p);
-    else if (st)
-      hipLaunchKernelGGL((fwd_kernel<64, false, true>), grid, block, 0, stream, p);
-    else
-      hipLaunchKernelGGL((fwd_kernel<64, false, false>), grid, block, 0, stream, p);
-  }
-  return hipGetLastError();
+  const int mode = (test || st) ? (bq2 ? 2 : 0) + (bk2 ? 1 : 0) : 0;
+  if (a.head_dim == 128) return launch_fm<128>(p, test, st, mode, grid, block, stream);
+  return launch_fm<64>(p, test, st, mode, grid, block, stream);
 }
 
 }  // namespace mala

@@ -14,6 +14,7 @@ struct FwdArgs {
   float* lse;
   int batch, heads_q, heads_kv, nq, nk, head_dim;
   int causal;
+  int block_q, block_k;  // decision tile, 64 or 128 each
   float scale;
   float tau;
   unsigned long long* counters;
@@ -33,6 +34,7 @@ struct BwdArgs {
   void* workspace;  // bwd_workspace_bytes(): per-block row terms + decision map
   int batch, heads_q, heads_kv, nq, nk, head_dim;
   int causal;
+  int block_q, block_k;  // decision tile, 64 or 128 each
   float scale;
   float tau;
   unsigned long long* counters;
@@ -50,6 +52,7 @@ struct DecodeArgs {
   float* part_u;  // [B][Hq][S][D]
   int batch, heads_q, heads_kv, nk, head_dim;
   int num_splits;
+  int block_k;  // decision tile keys, 64 or 128
   float scale;
   float tau;
   unsigned long long* counters;

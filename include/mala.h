@@ -31,8 +31,10 @@
  *     a misaligned pointer returns MALA_ERR_INVALID_ARG.
  *   - Query head h reads KV head h / (heads_q / heads_kv) (grouped-query
  *     attention; heads_q must be a multiple of heads_kv).
- *   - head_dim is 64 or 128. The decision tile is block_q x block_k; this
- *     build supports 64 x 64. Forward and backward must use the same tile
+ *   - head_dim is 64 or 128. The decision tile is block_q x block_k with
+ *     block_q, block_k in {64, 128} (other values: MALA_ERR_UNSUPPORTED);
+ *     the kernels compute on 64 x 64 tiles and a larger decision tile
+ *     decides its 64 x 64 parts together. Forward and backward must use the same tile
  *     (the nesting of Sec. 2.2 relies on one partition).
  *   - Scores are s = softmax_scale * <q, k> (the paper folds the scale into
  *     Q, Sec. 2.1); pass 1/sqrt(head_dim) for standard attention.
@@ -79,8 +81,8 @@ typedef struct {
    * 0: every query sees all seqlen_k keys, L_q = seqlen_k. Ignored by
    *    decode, which always uses L = seqlen_k (Sec. 2.1, decoding). */
   int32_t causal;
-  int32_t block_q;     /* decision tile rows; 64 */
-  int32_t block_k;     /* decision tile keys; 64 */
+  int32_t block_q;     /* decision tile rows: 64 or 128 (decode ignores it) */
+  int32_t block_k;     /* decision tile keys: 64 or 128 */
   float tau;           /* tolerance, >= 0; 0 never skips (Sec. 2.3: tau -> 0
                           recovers FullAttn); +inf allowed; NaN / < 0
                           rejected. Ignored by the fullattn_* entry points. */
@@ -93,9 +95,10 @@ typedef struct {
  *             [0] legal tiles tested, [1] retained tiles,
  *             [2] retained post-score key slots (valid rows x block_k per
  *                 retained tile: the count of Sec. 2.3 / Eq. 11),
- *             [3] V tiles loaded from HBM (forward and decode); dO tiles
- *                 loaded by the dK/dV pass (backward: one per retained
- *                 tile).
+ *             [3] 64-key V tiles loaded from HBM (forward and decode);
+ *                 64-row dO tiles loaded by the dK/dV pass (backward: one
+ *                 per legal 64 x 64 part of a retained tile).
+ *             [0]-[2] count decision tiles (block_q x block_k).
  *   decisions device uint8, one byte per tile, written 1 (retained) or
  *             0 (skipped) for every legal tile the call tests; other bytes
  *             are left untouched. Layout [batch][heads_q][Tr][Tc] for

@@ -61,7 +61,9 @@ def fwd(s, c, q=FAKE, fn="mala_fwd"):
     (shape(Nq=0, Nk=0), cfg(), m.MALA_ERR_INVALID_ARG),
     (shape(d=96), cfg(), m.MALA_ERR_UNSUPPORTED),
     (shape(d=0), cfg(), m.MALA_ERR_INVALID_ARG),
-    (shape(), cfg(bq=128, bk=128), m.MALA_ERR_UNSUPPORTED),
+    (shape(), cfg(bq=96, bk=64), m.MALA_ERR_UNSUPPORTED),
+    (shape(), cfg(bq=64, bk=256), m.MALA_ERR_UNSUPPORTED),
+    (shape(), cfg(bq=32, bk=32), m.MALA_ERR_UNSUPPORTED),
     (shape(), cfg(bq=0), m.MALA_ERR_INVALID_ARG),
     (shape(), cfg(tau=float("nan")), m.MALA_ERR_INVALID_ARG),
     (shape(), cfg(tau=-1.0), m.MALA_ERR_INVALID_ARG),
@@ -100,6 +102,10 @@ def test_valid_call_without_device_reports_device_error():
     assert fwd(shape(), cfg()) == m.MALA_ERR_DEVICE
     # causal with fewer queries than keys (prefill against a cache) is accepted
     assert fwd(shape(Nq=100, Nk=128), cfg()) == m.MALA_ERR_DEVICE
+    # decision tiles of 64 or 128 rows and keys
+    for bq in (64, 128):
+        for bk in (64, 128):
+            assert fwd(shape(), cfg(bq=bq, bk=bk)) == m.MALA_ERR_DEVICE
     assert fwd(shape(), cfg(tau=float("nan")), fn="fullattn_fwd") == m.MALA_ERR_DEVICE
 
 
@@ -157,6 +163,8 @@ def test_decode_validation():
     assert dec(shape(Nq=2, Nk=4096), cfg()) == m.MALA_ERR_INVALID_ARG
     assert dec(s, cfg(), S=0) == m.MALA_ERR_INVALID_ARG
     assert dec(s, cfg(), S=65) == m.MALA_ERR_INVALID_ARG  # more splits than tiles
+    # 128-key decision tiles: 32 of them in 4096 keys
+    assert dec(s, cfg(bk=128), S=33) == m.MALA_ERR_INVALID_ARG
     assert dec(s, cfg(), ws=None) == m.MALA_ERR_WORKSPACE
     assert dec(s, cfg(), nbytes=100) == m.MALA_ERR_WORKSPACE
     assert dec(s, cfg(tau=float("nan"))) == m.MALA_ERR_INVALID_ARG

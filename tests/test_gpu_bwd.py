@@ -22,12 +22,12 @@ def mala():
     return m
 
 
-def run_fwd_bwd(inp, tau, causal=True, dense=False):
+def run_fwd_bwd(inp, tau, causal=True, dense=False, bq=64, bk=64):
     m = mala()
     q, k, v, do = (bits_to_gpu(inp[x]) for x in ("q", "k", "v", "do"))
     B, Hq, Nq, d = q.shape
     Nk = k.shape[2]
-    Tr, Tc = -(-Nq // 64), -(-Nk // 64)
+    Tr, Tc = -(-Nq // bq), -(-Nk // bk)
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device="cuda")
     fst = m.Stats(torch.zeros(4, dtype=torch.int64, device="cuda"),
@@ -35,14 +35,15 @@ def run_fwd_bwd(inp, tau, causal=True, dense=False):
     bst = m.Stats(torch.zeros(4, dtype=torch.int64, device="cuda"),
                   torch.full((B, Hq, Tr, Tc), 255, dtype=torch.uint8, device="cuda"))
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(m.mala_bwd_workspace_bytes(q, k, causal=causal), dtype=torch.uint8,
-                     device="cuda")
+    ws = torch.empty(m.mala_bwd_workspace_bytes(q, k, causal=causal, block_q=bq, block_k=bk),
+                     dtype=torch.uint8, device="cuda")
+    t = {"block_q": bq, "block_k": bk}
     if dense:
-        m.fullattn_fwd(q, k, v, o, lse, causal=causal, stats=fst)
-        m.fullattn_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, causal=causal, stats=bst)
+        m.fullattn_fwd(q, k, v, o, lse, causal=causal, stats=fst, **t)
+        m.fullattn_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, causal=causal, stats=bst, **t)
     else:
-        m.mala_fwd(q, k, v, o, lse, causal=causal, tau=tau, stats=fst)
-        m.mala_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, causal=causal, tau=tau, stats=bst)
+        m.mala_fwd(q, k, v, o, lse, causal=causal, tau=tau, stats=fst, **t)
+        m.mala_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, causal=causal, tau=tau, stats=bst, **t)
     torch.cuda.synchronize()
     return {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv,
             "fdec": fst.decisions.cpu().numpy().astype(np.int8),
@@ -59,22 +60,23 @@ def _legal_sel(dec, sel):
     return m
 
 
-def run_bwd_given(inp, o, lse, tau, causal=True):
+def run_bwd_given(inp, o, lse, tau, causal=True, bq=64, bk=64):
     """The GPU backward alone, on given forward outputs (O as bf16 values,
     LSE as fp32 values)."""
     m = mala()
     q, k, v, do = (bits_to_gpu(inp[x]) for x in ("q", "k", "v", "do"))
     B, Hq, Nq, d = q.shape
-    Tr, Tc = -(-Nq // 64), -(-k.shape[2] // 64)
+    Tr, Tc = -(-Nq // bq), -(-k.shape[2] // bk)
     og = torch.from_numpy(np.ascontiguousarray(o, dtype=np.float32)).to(torch.bfloat16).cuda()
     lg = torch.from_numpy(np.ascontiguousarray(lse, dtype=np.float32)).cuda()
     assert np.array_equal(og.float().cpu().numpy(), np.asarray(o, dtype=np.float32))
     bst = m.Stats(torch.zeros(4, dtype=torch.int64, device="cuda"),
                   torch.full((B, Hq, Tr, Tc), 255, dtype=torch.uint8, device="cuda"))
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(m.mala_bwd_workspace_bytes(q, k, causal=causal), dtype=torch.uint8,
-                     device="cuda")
-    m.mala_bwd(q, k, v, og, lg, do, dq, dk, dv, ws, causal=causal, tau=tau, stats=bst)
+    ws = torch.empty(m.mala_bwd_workspace_bytes(q, k, causal=causal, block_q=bq, block_k=bk),
+                     dtype=torch.uint8, device="cuda")
+    m.mala_bwd(q, k, v, og, lg, do, dq, dk, dv, ws, causal=causal, tau=tau, stats=bst,
+               block_q=bq, block_k=bk)
     torch.cuda.synchronize()
     return {"dq": dq, "dk": dk, "dv": dv,
             "bdec": bst.decisions.cpu().numpy().astype(np.int8)}
@@ -107,7 +109,8 @@ def _fwd_rows(shape, fwd_sel):
     return m
 
 
-def compare_bwd(inp, tau, causal=True, sel_q=None, sel_k=None, fwd_sel=None, label=""):
+def compare_bwd(inp, tau, causal=True, sel_q=None, sel_k=None, fwd_sel=None, label="", bq=64,
+                bk=64):
     """Two checks of the backward.
     End to end (GPU forward, then GPU backward on its outputs): decisions,
     fidelity to the fp64 oracle (relative L2, with the D term for the stored
@@ -115,14 +118,15 @@ def compare_bwd(inp, tau, causal=True, sel_q=None, sel_k=None, fwd_sel=None, lab
     Backward alone (GPU backward on the oracle's bf16-model forward outputs,
     so that both sides form D from the same stored O): decisions, V1 and V2
     against the oracle's bf16-operand backward model."""
-    g = run_fwd_bwd(inp, tau, causal)
     q, k, v, do = (bits_to_f64(inp[x]) for x in ("q", "k", "v", "do"))
     G = q.shape[1] // k.shape[1]
-    print(f"[bwd {label}] q{q.shape} k{k.shape} tau={tau} causal={causal}", flush=True)
+    print(f"[bwd {label}] q{q.shape} k{k.shape} tau={tau} causal={causal} tile {bq}x{bk}",
+          flush=True)
+    g = run_fwd_bwd(inp, tau, causal, bq=bq, bk=bk)
 
     # --- oracle forward on the GPU's branch of ambiguous tiles ---
     def fwd(force, flags=O.EXACT):
-        return O.mala_fwd(q, k, v, tau, causal, 64, 64, round_flags=flags, force=force,
+        return O.mala_fwd(q, k, v, tau, causal, bq, bk, round_flags=flags, force=force,
                           sel=fwd_sel)
 
     ffree = fwd(None)
@@ -132,7 +136,7 @@ def compare_bwd(inp, tau, causal=True, sel_q=None, sel_k=None, fwd_sel=None, lab
     fbf = fwd(fex["dec"].copy(), O.BF16_FWD)
 
     def bwd(o_, lse_, flags, force=None):
-        return O.mala_bwd(q, k, v, o_, lse_, do, tau, causal, 64, 64, round_flags=flags,
+        return O.mala_bwd(q, k, v, o_, lse_, do, tau, causal, bq, bk, round_flags=flags,
                           force=force, sel_q=sel_q, sel_k=sel_k)
 
     rq = _rows_q(sel_q, q.shape)
@@ -160,7 +164,12 @@ def compare_bwd(inp, tau, causal=True, sel_q=None, sel_k=None, fwd_sel=None, lab
     # counters agree with the bitmaps: legal and kept tiles of the scoring pass, and
     # every kept (tile, key block) listed once by the dK/dV pass
     bc, fc = g["bcnt"], g["fcnt"]
-    assert bc[0] == int((gd >= 0).sum()) and bc[1] == int((gd == 1).sum()) and bc[3] == bc[1]
+    assert bc[0] == int((gd >= 0).sum()) and bc[1] == int((gd == 1).sum())
+    # the dK/dV pass loads dO once per legal 64 x 64 sub-tile of a kept tile
+    sub = _subtile_counts(q.shape[2], k.shape[2], bq, bk, causal)
+    assert bc[3] == int(((gd == 1) * sub[None, None]).sum())
+    rows = np.array([min(q.shape[2], (I + 1) * bq) - I * bq for I in range(gd.shape[2])])
+    assert bc[2] == int(((gd == 1) * rows[None, None, :, None]).sum()) * bk
     assert fc[0] == int((g["fdec"] >= 0).sum()) and fc[1] == int((g["fdec"] == 1).sum())
 
     # --- the backward alone, on the oracle's bf16-model forward outputs (the
@@ -169,7 +178,7 @@ def compare_bwd(inp, tau, causal=True, sel_q=None, sel_k=None, fwd_sel=None, lab
     rows = _fwd_rows(q.shape, fwd_sel)
     o_in = np.where(rows[..., None], fbf["o"], gpu_to_f64(g["o"]))
     lse_in = np.where(rows, fbf["lse"], g["lse"].cpu().numpy().astype(np.float64))
-    g2 = run_bwd_given(inp, o_in, lse_in, tau, causal)
+    g2 = run_bwd_given(inp, o_in, lse_in, tau, causal, bq=bq, bk=bk)
     b2, _, agree2, bflip2 = _settle_bwd(bwd, fbf["o"], fbf["lse"], g2["bdec"])
     b2bf = bwd(fbf["o"], fbf["lse"], O.BF16_BWD, b2["dec"].copy())
     b2mag = bwd(fbf["o"], fbf["lse"], O.BF16_BWD | O.ABS, b2["dec"].copy())
@@ -185,6 +194,20 @@ def compare_bwd(inp, tau, causal=True, sel_q=None, sel_k=None, fwd_sel=None, lab
         out[name + "_v2"] = r2
     out["g"] = g
     print({k_: v_ for k_, v_ in out.items() if k_ != "g"}, flush=True)
+    return out
+
+
+def _subtile_counts(Nq, Nk, bq, bk, causal):
+    """Legal 64 x 64 sub-tiles of every bq x bk decision tile (queries at the
+    end of the keys when causal)."""
+    off = Nk - Nq if causal else 0
+    tr, tc = -(-Nq // 64), -(-Nk // 64)
+    kq, kk = bq // 64, bk // 64
+    out = np.zeros((-(-Nq // bq), -(-Nk // bk)), dtype=np.int64)
+    for i in range(tr):
+        for j in range(tc):
+            if not causal or 64 * j <= 64 * i + 63 + off:
+                out[i // kq, j // kk] += 1
     return out
 
 
@@ -304,3 +327,22 @@ def test_backward_causal_chunk_against_cache(Nq, Nk, Hq, Hkv, d, tau):
     inp = {"q": np.ascontiguousarray(a["q"][:, :, Nk - Nq:]), "k": a["k"], "v": a["v"],
            "do": np.ascontiguousarray(a["do"][:, :, Nk - Nq:])}
     compare_bwd(inp, tau, causal=True, label=f"chunk{Nq}of{Nk}")
+
+
+@pytest.mark.parametrize("bq,bk", [(128, 128), (128, 64), (64, 128)])
+@pytest.mark.parametrize("N,Hq,Hkv,d,tau,causal", [
+    (777, 4, 2, 128, 1.0, True),     # ragged, GQA 2:1, odd number of 128-key tiles
+    (640, 3, 1, 64, 4.0, True),      # G = 3
+    (450, 2, 2, 128, 1.0, False),    # non-causal
+])
+def test_backward_decision_tile_128(bq, bk, N, Hq, Hkv, d, tau, causal):
+    """Decision tiles of 128 rows and / or 128 keys, end to end and on the
+    oracle's forward outputs, against the oracle run with the same tile."""
+    compare_bwd(_gen(800 + N + bq + bk, 1, Hq, Hkv, N, d, 8, local=True), tau, causal,
+                label=f"tile{bq}x{bk}", bq=bq, bk=bk)
+
+
+def test_backward_decision_tile_128_chunk_against_cache():
+    a = W.peaked(W.Spec(833, 1, 4, 2, 700, 128, 3.0, 8, local_bias=True),
+                 q_rows=list(range(600, 700)))
+    compare_bwd(a, 1.0, True, label="chunk128", bq=128, bk=128)

@@ -28,7 +28,7 @@ def decode_inputs(spec):
     return inp
 
 
-def run_decode(inp, tau, S, dense=False, with_stats=True):
+def run_decode(inp, tau, S, dense=False, with_stats=True, bk=64):
     m = mala()
     q, k, v = bits_to_gpu(inp["q"]), bits_to_gpu(inp["k"]), bits_to_gpu(inp["v"])
     B, Hq, d = q.shape
@@ -39,20 +39,21 @@ def run_decode(inp, tau, S, dense=False, with_stats=True):
     stats = None
     if with_stats:
         stats = m.Stats(torch.zeros(4, dtype=torch.int64, device="cuda"),
-                        torch.full((B, Hq, -(-Nk // 64)), 255, dtype=torch.uint8, device="cuda"))
+                        torch.full((B, Hq, -(-Nk // bk)), 255, dtype=torch.uint8, device="cuda"))
     if dense:
-        m.fullattn_decode(q, k, v, o, lse, S, ws, stats=stats)
+        m.fullattn_decode(q, k, v, o, lse, S, ws, stats=stats, block_k=bk)
     else:
-        m.mala_decode(q, k, v, o, lse, S, ws, tau=tau, stats=stats)
+        m.mala_decode(q, k, v, o, lse, S, ws, tau=tau, stats=stats, block_k=bk)
     torch.cuda.synchronize()
     dec = stats.decisions.cpu().numpy().astype(np.int8) if with_stats else None
     cnt = stats.counters.cpu().numpy() if with_stats else None
     return o, lse, dec, cnt
 
 
-def compare_decode(inp, tau, S, batches=None, label=""):
-    o, lse, dec, cnt = run_decode(inp, tau, S)
-    print(f"[decode {label}] q{inp['q'].shape} k{inp['k'].shape} tau={tau} S={S}", flush=True)
+def compare_decode(inp, tau, S, batches=None, label="", bk=64):
+    print(f"[decode {label}] q{inp['q'].shape} k{inp['k'].shape} tau={tau} S={S} block_k={bk}",
+          flush=True)
+    o, lse, dec, cnt = run_decode(inp, tau, S, bk=bk)
     bsel = slice(None) if batches is None else list(batches)
     q = bits_to_f64(inp["q"][bsel])
     k = bits_to_f64(inp["k"][bsel])
@@ -62,7 +63,7 @@ def compare_decode(inp, tau, S, batches=None, label=""):
     gd = dec[bsel]
 
     def run(force, flags=O.EXACT):
-        return O.mala_decode(q, k, v, S, tau, 64, round_flags=flags, force=force)
+        return O.mala_decode(q, k, v, S, tau, bk, round_flags=flags, force=force)
 
     free = run(None)
     legal = free["dec"] >= 0
@@ -81,6 +82,7 @@ def compare_decode(inp, tau, S, batches=None, label=""):
     assert np.isfinite(go).all() and np.isfinite(gl).all()
     if batches is None:
         assert cnt[0] == int((dec >= 0).sum()) and cnt[1] == int((dec == 1).sum())
+        assert cnt[2] == bk * cnt[1]
     return {"agree": agree, "v2": r2, "flipped": flipped, "dec": dec, "cnt": cnt}
 
 
@@ -166,7 +168,7 @@ def paged_inputs(seed, lens, Hq, Hkv, d, spare=5):
             "lens": np.array(lens, dtype=np.int32), "max_len": max_len}
 
 
-def run_decode_paged(pin, tau, S, dense=False, lens=None):
+def run_decode_paged(pin, tau, S, dense=False, lens=None, bk=64):
     m = mala()
     q = bits_to_gpu(pin["q"])
     kp, vp = bits_to_gpu(pin["kp"]), bits_to_gpu(pin["vp"])
@@ -178,12 +180,14 @@ def run_decode_paged(pin, tau, S, dense=False, lens=None):
     ws = torch.empty(m.mala_decode_paged_workspace_bytes(q, pin["max_len"], kp.shape[1], S),
                      dtype=torch.uint8, device="cuda")
     st = m.Stats(torch.zeros(4, dtype=torch.int64, device="cuda"),
-                 torch.full((B, Hq, table.shape[1]), 255, dtype=torch.uint8, device="cuda"))
+                 torch.full((B, Hq, -(-pin["max_len"] // bk)), 255, dtype=torch.uint8,
+                            device="cuda"))
     if dense:
-        m.fullattn_decode_paged(q, kp, vp, table, lens_g, pin["max_len"], o, lse, S, ws, stats=st)
+        m.fullattn_decode_paged(q, kp, vp, table, lens_g, pin["max_len"], o, lse, S, ws, stats=st,
+                                block_k=bk)
     else:
         m.mala_decode_paged(q, kp, vp, table, lens_g, pin["max_len"], o, lse, S, ws, tau=tau,
-                            stats=st)
+                            stats=st, block_k=bk)
     torch.cuda.synchronize()
     return o, lse, st.decisions.cpu().numpy().astype(np.int8), st.counters.cpu().numpy()
 
@@ -224,9 +228,11 @@ def test_decode_paged_varlen(tau, S):
     assert cnt[0] == legal_total and cnt[1] == kept_total
 
 
-def test_decode_paged_equals_contiguous():
+@pytest.mark.parametrize("bk", [64, 128])
+def test_decode_paged_equals_contiguous(bk):
     """Equal lengths and pages in order: the paged path computes exactly what
-    mala_decode computes on the contiguous caches (bitwise), MALA and dense."""
+    mala_decode computes on the contiguous caches (bitwise), MALA and dense,
+    for 64- and 128-key decision tiles."""
     m = mala()
     spec = W.Spec(43, 3, 8, 2, 777, 128, 3.0, 8)
     inp = decode_inputs(spec)
@@ -244,9 +250,10 @@ def test_decode_paged_equals_contiguous():
     pin = {"q": inp["q"], "kp": kp, "vp": vp, "table": table,
            "lens": np.full(B, N, dtype=np.int32), "max_len": N}
     for dense in (False, True):
-        o1, l1, _, _ = run_decode(inp, 1.0, 4, dense=dense)
-        o2, l2, _, _ = run_decode_paged(pin, 1.0, 4, dense=dense)
+        o1, l1, d1, _ = run_decode(inp, 1.0, 4, dense=dense, bk=bk)
+        o2, l2, d2, _ = run_decode_paged(pin, 1.0, 4, dense=dense, bk=bk)
         assert torch.equal(o1, o2) and torch.equal(l1, l2)
+        assert np.array_equal(d1, d2)
 
 
 def test_decode_paged_bad_entries_give_nan_for_that_sequence():
@@ -264,3 +271,25 @@ def test_decode_paged_bad_entries_give_nan_for_that_sequence():
     o, l, _, _ = run_decode_paged(pin2, 1.0, 2)
     assert torch.isnan(o[2].float()).all() and torch.isnan(l[2]).all()
     assert torch.equal(o[0], o_ref[0]) and torch.equal(o[1], o_ref[1])
+
+
+@pytest.mark.parametrize("Nk,Hq,Hkv,d,S", [
+    (1000, 8, 2, 128, 3),      # ragged last 128-key tile (its upper half empty)
+    (4097, 8, 1, 128, 7),      # one key in the last tile
+    (3000, 6, 2, 64, 5),       # G = 3
+    (129, 4, 4, 128, 2),       # two decision tiles, one split each
+])
+@pytest.mark.parametrize("tau", [0.0, 1.0, 4.0])
+def test_decode_decision_tile_128(Nk, Hq, Hkv, d, S, tau):
+    """1 x 128 decision tiles (split boundaries on 128 keys): against the
+    oracle's decode with the same tile."""
+    spec = W.Spec(960 + Nk, 2, Hq, Hkv, Nk, d, 3.0, 8 if Nk > 200 else 0)
+    compare_decode(decode_inputs(spec), tau, S, label=f"Nk{Nk}-bk128", bk=128)
+
+
+def test_decode_tile_128_dense_identity():
+    inp = decode_inputs(W.Spec(979, 2, 8, 2, 3000, 128, 3.0, 16))
+    a = run_decode(inp, 0.0, 6, bk=128)
+    b = run_decode(inp, 0.0, 6, dense=True, bk=128)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    assert (a[2][a[2] >= 0] == 1).all()

@@ -26,22 +26,22 @@ def mala():
     return M
 
 
-def run_fwd(inp, tau, causal=True, dense=False, with_stats=True, nk_override=None):
+def run_fwd(inp, tau, causal=True, dense=False, with_stats=True, nk_override=None, bq=64, bk=64):
     m = mala()
     q, k, v = bits_to_gpu(inp["q"]), bits_to_gpu(inp["k"]), bits_to_gpu(inp["v"])
     B, Hq, Nq, d = q.shape
     Nk = k.shape[2]
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device="cuda")
-    Tr, Tc = -(-Nq // 64), -(-Nk // 64)
+    Tr, Tc = -(-Nq // bq), -(-Nk // bk)
     stats = None
     if with_stats:
         stats = m.Stats(torch.zeros(4, dtype=torch.int64, device="cuda"),
                         torch.full((B, Hq, Tr, Tc), 255, dtype=torch.uint8, device="cuda"))
     if dense:
-        m.fullattn_fwd(q, k, v, o, lse, causal=causal, stats=stats)
+        m.fullattn_fwd(q, k, v, o, lse, causal=causal, stats=stats, block_q=bq, block_k=bk)
     else:
-        m.mala_fwd(q, k, v, o, lse, causal=causal, tau=tau, stats=stats)
+        m.mala_fwd(q, k, v, o, lse, causal=causal, tau=tau, stats=stats, block_q=bq, block_k=bk)
     torch.cuda.synchronize()
     dec = None
     cnt = None
@@ -51,14 +51,15 @@ def run_fwd(inp, tau, causal=True, dense=False, with_stats=True, nk_override=Non
     return o, lse, dec, cnt
 
 
-def compare_fwd(inp, tau, causal=True, sel=None, label=""):
+def compare_fwd(inp, tau, causal=True, sel=None, label="", bq=64, bk=64):
     q, k, v = bits_to_f64(inp["q"]), bits_to_f64(inp["k"]), bits_to_f64(inp["v"])
-    o, lse, dec, cnt = run_fwd(inp, tau, causal)
+    print(f"[fwd {label}] q{tuple(q.shape)} k{tuple(k.shape)} tau={tau} causal={causal} "
+          f"tile {bq}x{bk}", flush=True)
+    o, lse, dec, cnt = run_fwd(inp, tau, causal, bq=bq, bk=bk)
     go, gl = gpu_to_f64(o), lse.cpu().numpy().astype(np.float64)
-    print(f"[fwd {label}] q{tuple(q.shape)} k{tuple(k.shape)} tau={tau} causal={causal}", flush=True)
 
     def run(force, flags=O.EXACT):
-        return O.mala_fwd(q, k, v, tau, causal, 64, 64, round_flags=flags, force=force, sel=sel)
+        return O.mala_fwd(q, k, v, tau, causal, bq, bk, round_flags=flags, force=force, sel=sel)
 
     free = run(None)
     legal = _legal(free["dec"], sel)
@@ -81,9 +82,13 @@ def compare_fwd(inp, tau, causal=True, sel=None, label=""):
     assert np.abs(gl[rows[:3]] - ex["lse"][rows[:3]]).max() <= LSE_TOL
     assert np.isfinite(go[rows]).all() and np.isfinite(gl[rows[:3]]).all()
     if sel is None:
-        # counters agree with the bitmap
+        # counters agree with the bitmap: legal and kept tiles, and block_k
+        # slots for each valid row of a kept tile (Eq. 11)
         assert cnt[0] == int((dec >= 0).sum())
         assert cnt[1] == int((dec == 1).sum())
+        Nq = q.shape[2]
+        rows = np.array([min(Nq, (I + 1) * bq) - I * bq for I in range(dec.shape[2])])
+        assert cnt[2] == int(((dec == 1) * rows[None, None, :, None]).sum()) * bk
     return {"agree": agree, "v2": r2, "l2": rl2, "flipped": flipped, "dec": dec, "ora": ex, "o": o, "lse": lse}
 
 
@@ -203,3 +208,48 @@ def test_forward_causal_chunk_against_cache(Nq, Nk, Hq, Hkv, d, tau):
     a = W.peaked(W.Spec(900 + Nq, 1, Hq, Hkv, Nk, d, 3.0, 6), want_do=False)
     inp = {"q": np.ascontiguousarray(a["q"][:, :, Nk - Nq:]), "k": a["k"], "v": a["v"]}
     compare_fwd(inp, tau, causal=True, label=f"chunk{Nq}of{Nk}")
+
+
+@pytest.mark.parametrize("bq,bk", [(128, 128), (128, 64), (64, 128)])
+@pytest.mark.parametrize("N,Hq,Hkv,d,tau,causal", [
+    (777, 4, 2, 128, 1.0, True),     # ragged: partial 128-row and 128-key tiles
+    (1100, 8, 1, 128, 1.0, True),    # GQA 8:1
+    (640, 3, 1, 64, 4.0, True),      # G = 3 (one head, four query blocks per workgroup)
+    (500, 2, 2, 128, 1.0, False),    # non-causal
+])
+def test_forward_decision_tile_128(bq, bk, N, Hq, Hkv, d, tau, causal):
+    """Decision tiles of 128 rows and / or 128 keys: decisions, counters and
+    values against the oracle run with the same tile (its decisions depend on
+    the tile, Sec. 2.2)."""
+    r = compare_fwd(_gen(700 + N + bq + bk, 1, Hq, Hkv, N, d, 8, local=True), tau, causal,
+                    label=f"tile{bq}x{bk}", bq=bq, bk=bk)
+    assert r["agree"] >= 0.99
+
+
+def test_forward_decision_tile_128_chunk_against_cache():
+    """A chunk of 100 queries at the end of 700 keys with 128 x 128 tiles:
+    the shifted staircase with partial coarse tiles on both axes."""
+    a = W.peaked(W.Spec(733, 1, 4, 2, 700, 128, 3.0, 8, local_bias=True), q_rows=list(range(600, 700)),
+                 want_do=False)
+    compare_fwd(a, 1.0, True, label="chunk128", bq=128, bk=128)
+
+
+def test_forward_tile_128_tau0_is_dense():
+    inp = _gen(741, 1, 4, 2, 600, 128, 8)
+    for bq, bk in ((128, 128), (64, 128), (128, 64)):
+        o1, l1, _, c1 = run_fwd(inp, 0.0, bq=bq, bk=bk)
+        o2, l2, _, _ = run_fwd(inp, 0.0, dense=True, with_stats=False)
+        # every tile kept: the same sums as the dense kernel in the same order
+        assert c1[0] == c1[1]
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("N,Hkv,bq,bk", [(3000, 2, 128, 128), (3000, 2, 64, 128), (8192, 1, 64, 128)])
+def test_forward_tile_128_upper_tile_kept_late(N, Hkv, bq, bk):
+    """128-key tiles whose upper half fails the test against the tile's
+    state while the lower half passes (the local bias makes this frequent at
+    these lengths): the pair is kept, its upper half scored again and both
+    halves updated against one reference maximum. Values and decisions
+    against the oracle with the same tile."""
+    inp = _gen(1700 + N + 64, 1, 2, Hkv, N, 128, 64, local=True)
+    compare_fwd(inp, 4.0, True, label=f"late{N}-{bq}x{bk}", bq=bq, bk=bk)
