@@ -15,7 +15,9 @@
 //      they neither pass the test nor contribute, P = 0).
 //   2. bwd_score: key-major scoring of every legal tile (S^T = K Q^T on
 //      32x32x16 MFMA, max-then-compare test per query column); writes the
-//      decision byte map and the kept-item count of every key block.
+//      decision byte map and the kept-item count of every key block. With
+//      decision tiles larger than 64 x 64, bwd_coarsen then ORs each tile's
+//      64 x 64 parts and recounts the kept items.
 //   3. bwd_pair: pairs the key blocks for the dK/dV pass by kept-item count
 //      (blocks most items keep, such as an attention sink or a retrieval
 //      hub, keep nearly the same items and are paired with each other).

@@ -140,7 +140,8 @@ size_t mala_bwd_workspace_bytes(const mala_shape* shape, const mala_config* cfg)
 /* MALA backward (Algorithm 2; Eq. 4; the backward part of Appendix A.1).
  * A key-major scoring pass recomputes Q.K for every legal tile and skips a
  * tile when every legal entry has s - z_q < log(tau / L_q), with z = the
- * forward's LSE; the decisions are stored in the workspace. A key-major
+ * forward's LSE (a tile of 128 rows or keys is kept iff one of its 64 x 64
+ * parts is); the decisions are stored in the workspace. A key-major
  * pass over pairs of key blocks then runs, for the kept tiles only,
  * P = exp(s - z), dP = dO V^T, dS = P o (dP - rowsum(O o dO)) and the dV and
  * dK products, and a query-major pass forms dQ over the kept tiles
