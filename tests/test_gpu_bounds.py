@@ -3,8 +3,8 @@
 Each output tensor and the workspace sit in the middle of a larger device
 buffer whose guard regions hold a fill pattern: after the call the guards
 must be untouched and the inputs unchanged. Each call runs twice, over two
-different fill patterns, and must give the same outputs (up to the
-rounding order of dQ's atomics), so that no output element is left as it was
+different fill patterns, and must give the same outputs bit for bit (every
+sum runs in a fixed order), so that no output element is left as it was
 found. Shapes are ragged (partial tiles, rectangular causal, paged caches with
 lengths that end mid-page) so that every tail path is exercised."""
 import math
@@ -50,19 +50,20 @@ def _inputs(seed, B, Hq, Hkv, Nq, Nk, d):
     return {x: bits_to_gpu(inp[x]) for x in ("q", "k", "v", "do")}
 
 
-def _prefill(m, t, causal, tau, dense, fill):
+def _prefill(m, t, causal, tau, dense, fill, tile=(64, 64)):
     q, k, v, do = t["q"], t["k"], t["v"], t["do"]
     B, Hq, Nq, d = q.shape
     o = Guarded(q.shape, torch.bfloat16, fill)
     lse = Guarded((B, Hq, Nq), torch.float32, fill)
     dq, dk, dv = (Guarded(x.shape, torch.bfloat16, fill) for x in (q, k, v))
-    ws = Guarded((m.mala_bwd_workspace_bytes(q, k, causal=causal),), torch.uint8, fill)
+    tk = {"block_q": tile[0], "block_k": tile[1]}
+    ws = Guarded((m.mala_bwd_workspace_bytes(q, k, causal=causal, **tk),), torch.uint8, fill)
     if dense:
-        m.fullattn_fwd(q, k, v, o.t, lse.t, causal=causal)
-        m.fullattn_bwd(q, k, v, o.t, lse.t, do, dq.t, dk.t, dv.t, ws.t, causal=causal)
+        m.fullattn_fwd(q, k, v, o.t, lse.t, causal=causal, **tk)
+        m.fullattn_bwd(q, k, v, o.t, lse.t, do, dq.t, dk.t, dv.t, ws.t, causal=causal, **tk)
     else:
-        m.mala_fwd(q, k, v, o.t, lse.t, causal=causal, tau=tau)
-        m.mala_bwd(q, k, v, o.t, lse.t, do, dq.t, dk.t, dv.t, ws.t, causal=causal, tau=tau)
+        m.mala_fwd(q, k, v, o.t, lse.t, causal=causal, tau=tau, **tk)
+        m.mala_bwd(q, k, v, o.t, lse.t, do, dq.t, dk.t, dv.t, ws.t, causal=causal, tau=tau, **tk)
     torch.cuda.synchronize()
     return {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv, "ws": ws}
 
@@ -73,24 +74,22 @@ def _prefill(m, t, causal, tau, dense, fill):
     (1, 4, 4, 300, 450, 128, False),   # non-causal rectangular
     (1, 8, 1, 65, 65, 128, True),      # one row past a tile, G = 8
 ])
-@pytest.mark.parametrize("dense", [False, True])
-def test_prefill_writes_only_its_outputs(B, Hq, Hkv, Nq, Nk, d, causal, dense):
+@pytest.mark.parametrize("dense,tile", [(False, (64, 64)), (True, (64, 64)), (False, (128, 128))])
+def test_prefill_writes_only_its_outputs(B, Hq, Hkv, Nq, Nk, d, causal, dense, tile):
     m = mala()
     t = _inputs(900 + Nq, B, Hq, Hkv, Nq, Nk, d)
     before = {x: y.clone() for x, y in t.items()}
     print(f"[bounds] prefill B{B} Hq{Hq} Hkv{Hkv} Nq{Nq} Nk{Nk} d{d} causal={causal} "
-          f"dense={dense}", flush=True)
-    r1 = _prefill(m, t, causal, 1.0, dense, 0xA5)
-    r2 = _prefill(m, t, causal, 1.0, dense, 0x5A)
+          f"dense={dense} tile={tile}", flush=True)
+    r1 = _prefill(m, t, causal, 1.0, dense, 0xA5, tile)
+    r2 = _prefill(m, t, causal, 1.0, dense, 0x5A, tile)
     for name in ("o", "lse", "dq", "dk", "dv", "ws"):
         assert r1[name].guards_intact() and r2[name].guards_intact(), name
     for x in t:
         assert torch.equal(t[x], before[x]), f"input {x} changed"
-    for name in ("o", "lse", "dk", "dv"):
+    for name in ("o", "lse", "dq", "dk", "dv"):
         assert torch.equal(r1[name].t, r2[name].t), name
-    dq1, dq2 = r1["dq"].t.float(), r2["dq"].t.float()
-    assert torch.isfinite(dq1).all() and torch.isfinite(r1["o"].t.float()).all()
-    assert (dq1 - dq2).abs().max().item() <= 1e-2 * max(1.0, dq1.abs().max().item())
+    assert torch.isfinite(r1["dq"].t.float()).all() and torch.isfinite(r1["o"].t.float()).all()
 
 
 def _decode_inputs(seed, B, Hq, Hkv, Nk, d):
@@ -104,9 +103,10 @@ def _decode_inputs(seed, B, Hq, Hkv, Nk, d):
     (2, 4, 4, 65, 64, 2),
     (1, 8, 1, 4097, 128, 7),
 ])
-@pytest.mark.parametrize("dense", [False, True])
-def test_decode_writes_only_its_outputs(B, Hq, Hkv, Nk, d, S, dense):
+@pytest.mark.parametrize("dense,bk", [(False, 64), (True, 64), (False, 128)])
+def test_decode_writes_only_its_outputs(B, Hq, Hkv, Nk, d, S, dense, bk):
     m = mala()
+    S = min(S, -(-Nk // bk))  # a split owns at least one decision tile
     q, k, v = _decode_inputs(950 + Nk, B, Hq, Hkv, Nk, d)
     before = [x.clone() for x in (q, k, v)]
     print(f"[bounds] decode B{B} Hq{Hq} Hkv{Hkv} Nk{Nk} d{d} S{S} dense={dense}", flush=True)
@@ -116,9 +116,9 @@ def test_decode_writes_only_its_outputs(B, Hq, Hkv, Nk, d, S, dense):
         lse = Guarded((B, Hq), torch.float32, fill)
         ws = Guarded((m.mala_decode_workspace_bytes(q, k, S),), torch.uint8, fill)
         if dense:
-            m.fullattn_decode(q, k, v, o.t, lse.t, S, ws.t)
+            m.fullattn_decode(q, k, v, o.t, lse.t, S, ws.t, block_k=bk)
         else:
-            m.mala_decode(q, k, v, o.t, lse.t, S, ws.t, tau=1.0)
+            m.mala_decode(q, k, v, o.t, lse.t, S, ws.t, tau=1.0, block_k=bk)
         torch.cuda.synchronize()
         assert o.guards_intact() and lse.guards_intact() and ws.guards_intact()
         outs.append((o.t.clone(), lse.t.clone()))

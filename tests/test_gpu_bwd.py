@@ -266,11 +266,12 @@ def test_backward_dense_identity_and_determinism():
     a = run_fwd_bwd(inp, 0.0)
     b = run_fwd_bwd(inp, 0.0, dense=True)
     c = run_fwd_bwd(inp, 0.0)
-    # dK, dV accumulate in registers: bitwise repeatable and equal to dense
-    assert torch.equal(a["dk"], b["dk"]) and torch.equal(a["dv"], b["dv"])
-    assert torch.equal(a["dk"], c["dk"]) and torch.equal(a["dv"], c["dv"])
-    # dQ sums fp32 atomics in arbitrary order: equal up to rounding
-    assert (a["dq"].float() - c["dq"].float()).abs().max().item() < 1e-2
+    # every gradient is summed in a fixed order (dK, dV in registers or in
+    # segment partials added in index order, dQ query-major without atomics):
+    # bitwise repeatable, and at tau = 0 equal to the dense path
+    for x in ("dq", "dk", "dv"):
+        assert torch.equal(a[x], c[x]), x
+        assert torch.equal(a[x], b[x]), x
 
 
 def test_cfg2_forward_backward_full():
