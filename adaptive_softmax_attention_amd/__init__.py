@@ -60,6 +60,11 @@ class Stats:
         self.decisions = decisions
 
     def _c(self):
+        for t, name in ((self.counters, "stats.counters"), (self.decisions, "stats.decisions")):
+            if t is not None:
+                if not t.is_cuda or not t.is_contiguous():
+                    raise ValueError(f"{name}: a contiguous device tensor is required")
+                _on_current_device(t, name)
         return _CStats(self.counters.data_ptr() if self.counters is not None else None,
                        self.decisions.data_ptr() if self.decisions is not None else None)
 
@@ -127,6 +132,15 @@ def _stream(stream):
     return torch.cuda.current_stream().cuda_stream
 
 
+def _on_current_device(t, name):
+    """The library launches on the current device: a tensor elsewhere would
+    hand it a pointer that device cannot use."""
+    import torch
+    cur = torch.cuda.current_device()
+    if t.device.index is not None and t.device.index != cur:
+        raise ValueError(f"{name}: on {t.device}, but the current device is cuda:{cur}")
+
+
 def _check(t, name, dtype, shape):
     import torch
     if t is None:
@@ -135,6 +149,7 @@ def _check(t, name, dtype, shape):
         raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
     if t.device.type != "cuda":
         raise ValueError(f"{name}: must be on the GPU")
+    _on_current_device(t, name)
     if not t.is_contiguous():
         raise ValueError(f"{name}: must be contiguous")
     if tuple(t.shape) != tuple(shape):
@@ -203,6 +218,7 @@ def _bwd(name, q, k, v, o, lse, dout, dq, dk, dv, workspace, causal, tau, block_
     _check(lse, "lse", torch.float32, (B, Hq, Nq))
     if workspace is None or not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace: a contiguous device tensor is required")
+    _on_current_device(workspace, "workspace")
     shp = make_shape(q, k)
     cfg = make_config(causal, tau, block_q, block_k, softmax_scale, d)
     st = stats._c() if stats is not None else None
@@ -251,6 +267,7 @@ def _decode(name, q, k_cache, v_cache, o, lse, num_splits, workspace, tau, block
     _check(lse, "lse", torch.float32, (B, Hq))
     if workspace is None or not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace: a contiguous device tensor is required")
+    _on_current_device(workspace, "workspace")
     shp = make_shape(q, k_cache, decode=True)
     cfg = make_config(False, tau, 64, block_k, softmax_scale, d)
     st = stats._c() if stats is not None else None
@@ -292,6 +309,7 @@ def _decode_paged(name, q, k_pages, v_pages, block_table, cache_lens, max_len, o
     _check(lse, "lse", torch.float32, (B, Hq))
     if workspace is None or not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace: a contiguous device tensor is required")
+    _on_current_device(workspace, "workspace")
     shp = Shape(B, Hq, Hkv, 1, int(max_len), d)
     cfg = make_config(False, tau, 64, block_k, softmax_scale, d)
     st = stats._c() if stats is not None else None

@@ -236,3 +236,12 @@ def test_misaligned_pointers_are_rejected():
         assert L.mala_decode_paged(ctypes.byref(sd), ctypes.byref(cfg(causal=0)), FAKE, FAKE, FAKE,
                                    table, lens, 8, FAKE, FAKE, 4, FAKE, 1 << 40, None,
                                    None) == m.MALA_ERR_INVALID_ARG
+
+
+def test_stats_tensors_must_be_device_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        m.Stats(torch.zeros(4, dtype=torch.int64))._c()
+    with pytest.raises(ValueError):
+        m.Stats(None, torch.zeros(8, dtype=torch.uint8))._c()
+    assert m.Stats()._c().counters is None
