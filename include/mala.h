@@ -176,9 +176,9 @@ int32_t mala_decode_default_splits(const mala_shape* shape);
  * fresh (m, l), visits its tiles last-to-first and tests each head's row
  * against its own partial normaliser; the partial (m, l, u) are merged with
  * the normaliser-aware reduction. Every cached key is scored; a V tile is
- * read only if some query head of the KV group retains it. This build
- * supports up to 8 query heads per KV head here (else MALA_ERR_UNSUPPORTED)
- * and requires 1 <= num_splits <= Tc. */
+ * read only if some query head of the KV group retains it. Decode supports
+ * up to 8 query heads per KV head (else MALA_ERR_UNSUPPORTED) and requires
+ * 1 <= num_splits <= Tc. */
 int mala_decode(const mala_shape* shape, const mala_config* cfg, const void* q,
                 const void* k_cache, const void* v_cache, void* o, float* lse,
                 int32_t num_splits, void* workspace, size_t workspace_bytes,
