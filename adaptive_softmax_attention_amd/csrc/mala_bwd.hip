@@ -981,7 +981,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
       const int s = s0 + lane;
       const int row = s / KCH, pc = s % KCH;
       const int kk = min(j * 64 + row, p.nk - 1);
-      async_copy16(base + (size_t)kk * D + ((pc ^ dsw(row)) & (KCH - 1)) * 8, slot + s0 * 8);
+      async_copy16(base + (size_t)kk * D + ((pc ^ dqswz<D>(row)) & (KCH - 1)) * 8, slot + s0 * 8);
     }
   };
 
@@ -1006,7 +1006,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
           // MFMA row l16 of key subtile 2kc + x holds key qperm(2kc + x, l16)
           const int kr = qperm(2 * kc + x, l16);
           const int ch = 4 * dc + g4;
-          const int off = kr * D + ((ch ^ dsw(kr)) & (KCH - 1)) * 8;
+          const int off = kr * D + ((ch ^ dqswz<D>(kr)) & (KCH - 1)) * 8;
           const bf16x8 ak = *(const bf16x8*)(kt + off);
           const bf16x8 av = *(const bf16x8*)(vt + off);
 #pragma unroll
@@ -1047,7 +1047,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
           const int row = 32 * kc + 8 * g4 + 4 * hh + (l16 >> 2);
           const int col = 16 * ds + 4 * (l16 & 3);
           t2[hh] =
-              lds_read_tr4(kt + row * D + (((col >> 3) ^ dsw(row)) & (KCH - 1)) * 8 + (col & 7));
+              lds_read_tr4(kt + row * D + (((col >> 3) ^ dqswz<D>(row)) & (KCH - 1)) * 8 + (col & 7));
         }
         const bf16x8 a = join_tr(t2[0], t2[1]);
 #pragma unroll

@@ -253,24 +253,6 @@ __device__ __forceinline__ bf16x8 join_tr(const short4v& lo, const short4v& hi) 
 }
 
 // --- LDS swizzles -----------------------------------------------------------
-// K tile in LDS: [64 keys][D] bf16, 16-byte chunks XOR-swizzled per key so
-// that the eight lanes of one read phase (keys 0-3 and 8-11 of a 16-key
-// group, same column chunk) hit distinct bank groups.
-__device__ __forceinline__ int k_swz(int key) {
-  return (key & 3) | ((key & 8) >> 1) | ((key & 4) << 1);
-}
-// V^T tile in LDS: [D][64 keys] bf16 (128 B rows of eight 16-byte chunks).
-__device__ __forceinline__ int v_swz(int d) { return (d ^ (d >> 3)) & 7; }
-// Row-major tiles read with the transposing read (4 consecutive rows x 2
-// chunks per 16-lane group): even row offsets keep the 8 chunks distinct.
-__device__ __forceinline__ int tr_swz(int row) { return (row << 1) ^ ((row >> 3) & 1); }
-// Tiles read both ways: row-major MFMA operand reads whose 16 rows are the
-// permuted set 32a + 8(R/4) + 4c + R%4 (R = 0..15), and transposing reads of
-// 4 consecutive rows x 16 columns per 16-lane group. Chunk bits 1-3 follow
-// row bits 0, 1, 3 (distinct chunks for the transposing reads) and bit 0
-// row bits 3 ^ 4 (distinct for the 8- and 16-row groups of the row-major
-// reads); with 256-byte rows (d = 128) both access kinds are free of bank
-// conflicts for 32 or 64 four-byte banks.
 // Tiles of the 32x32 products ([64 rows][D] bf16, 16-byte chunks XORed per
 // row). K-type tiles are read row-major by 32 consecutive rows per
 // instruction (one chunk each); their swizzle makes any 16 consecutive rows
@@ -304,8 +286,22 @@ __device__ __forceinline__ int qswz32(int row) {
     return (2 * (row & 1)) ^ (4 * ((row >> 1) & 1)) ^ ((row >> 2) & 1) ^ (2 * ((row >> 3) & 1));
 }
 
-__device__ __forceinline__ int dsw(int row) {
-  return (((row >> 3) ^ (row >> 4)) & 1) | ((row & 3) << 1) | (((row >> 3) & 1) << 3);
+// Tiles of the 16x16 products read both ways (the K and V tiles of the dQ
+// pass): row-major operand reads whose 16 rows per lane group are the
+// permuted set 32a + 8(R/4) + 4c + R%4 (R = 0..15, one chunk per lane group),
+// and transposing reads of 4 consecutive rows x 16 columns per 16-lane group.
+// Measured on gfx950 (bank-conflict counter, each access kind alone): the
+// transposing reads go in 32-lane phases over 64 banks, and a 16-byte read
+// serves, per half wave, the lanes whose bits 2-4 have equal parity
+// together. For d = 128 chunk bits 1-3 follow row bits 0, 1, 3; for d = 64
+// chunk bits 1-2 follow row bits 1, 3. Both access kinds are then free of
+// bank conflicts.
+template <int D>
+__device__ __forceinline__ int dqswz(int row) {
+  if constexpr (D == 128)
+    return ((row & 3) << 1) | (((row >> 3) & 1) << 3);
+  else
+    return (((row >> 1) & 1) << 1) | (((row >> 3) & 1) << 2);
 }
 
 }  // namespace mala
