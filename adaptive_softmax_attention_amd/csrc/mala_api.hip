@@ -2,9 +2,11 @@
 // and dispatch to the kernels. Every argument is checked on the host before
 // the first HIP call, so each error path returns a status without touching
 // the device.
+#include <limits.h>
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <atomic>
@@ -65,6 +67,22 @@ int check_device() {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? MALA_OK : MALA_ERR_LAUNCH; }
 
+// Bound on the kernels' waits for one another, in polls: far beyond any
+// legal schedule (a poll takes at least tens of cycles, so 2^22 of them
+// last tens of milliseconds, against microseconds for a legal wait). The
+// environment variable MALA_WAIT_BOUND overrides it for tests of the
+// failure path (0 makes every wait give up at once); a malformed value is
+// ignored.
+int wait_bound() {
+  constexpr int kDefault = 1 << 22;
+  const char* s = getenv("MALA_WAIT_BOUND");
+  if (!s || !*s) return kDefault;
+  char* end = nullptr;
+  const long long v = strtoll(s, &end, 10);
+  if (!end || *end != '\0' || v < 0) return kDefault;
+  return v > INT_MAX ? INT_MAX : (int)v;
+}
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // The kernels move bf16 rows in 16-byte vectors and the workspace in float4
@@ -112,6 +130,7 @@ int fwd_common(const mala_shape* shape, const mala_config* cfg, const void* q, c
   a.block_k = cfg->block_k;
   a.scale = cfg->softmax_scale;
   a.tau = test ? cfg->tau : 0.f;
+  a.spin = wait_bound();
   a.counters = stats ? stats->counters : nullptr;
   a.decisions = stats ? stats->decisions : nullptr;
   return launch_status(mala::launch_fwd(a, test, (hipStream_t)stream));
@@ -170,6 +189,7 @@ int bwd_common(const mala_shape* shape, const mala_config* cfg, const void* q, c
   a.block_k = cfg->block_k;
   a.scale = cfg->softmax_scale;
   a.tau = test ? cfg->tau : 0.f;
+  a.spin = wait_bound();
   a.counters = stats ? stats->counters : nullptr;
   a.decisions = stats ? stats->decisions : nullptr;
   return launch_status(mala::launch_bwd(a, test, (hipStream_t)stream));

@@ -33,6 +33,12 @@
 //      once, in bf16, with no atomics and no fp32 accumulator in memory.
 // The dense path fills the decision map with ones instead of scoring and
 // pairs blocks 2p, 2p + 1 without segments.
+//
+// The scoring pass's waves wait on each other through LDS flags. Every wait
+// is bounded (BwdParams::spin polls); a wait that reaches the bound ends all
+// waits of its workgroup and sets the status word at the start of the
+// workspace, and the passes that write dQ, dK and dV then write NaN
+// everywhere instead of values, so a give-up can never pass for a result.
 #include <type_traits>
 
 #include "mala_common.h"
@@ -41,15 +47,18 @@
 namespace mala {
 namespace {
 
-constexpr int kRowInfo = 256;  // floats of row terms per 64-row block
 // The dK/dV pass splits a pair's (query block, query head) items into at
-// most kSegMax equal segments, one workgroup each, about one per kSegKept
-// items the pair keeps, so that a key block that every row keeps (an
-// attention sink) does not serialise the pass; the segments' fp32 partial
-// sums are added in a fixed order by the finalize kernel (deterministic, no
-// atomics).
+// most kSegMax equal segments, one workgroup each, so that a key block that
+// every row keeps (an attention sink) does not serialise the pass; the
+// segments' fp32 partial sums are added in a fixed order by the finalize
+// kernel (deterministic, no atomics). A pair keeping `kept` items gets
+// min(kSegMax, ceil(kept / Lseg)) segments with Lseg = max(kSegKept,
+// ceil(K / npair)), K = the items all key blocks of the (batch, KV head)
+// keep. A pair with more than one segment keeps more than Lseg items, so its
+// segment count is below 2 kept / Lseg and all such pairs together hold
+// fewer than 2 K / Lseg <= 2 npair segments: the partials need 2 npair
+// slots per (batch, KV head), whatever the decisions.
 constexpr int kSegKept = 512;
-constexpr int kSegMax = 8;
 
 struct BwdParams {
   const __bf16* q;
@@ -61,9 +70,11 @@ struct BwdParams {
   __bf16* dq;
   __bf16* dk;
   __bf16* dv;
+  int* status;     // workspace word: 0, or 1 once a bounded wait gave up
+  int spin;        // bound on every wait of the scoring pass (polls)
   float* rowinfo;  // [B*Hq*Tr][kRowInfo]
   uint8_t* dmap;   // backward decisions, see dmap_index()
-  float* part;     // [B*Hkv*Tc][kSegMax][2][64][D] fp32 partial dK, dV
+  float* part;     // [B*Hkv][2 npair slots][2 blocks][2][64][D] fp32 partial dK, dV
   int batch, heads_q, heads_kv, nq, nk, group;
   int causal;
   int off;   // causal: query q sits at key position q + off (off = nk - nq >= 0)
@@ -76,7 +87,7 @@ struct BwdParams {
   int hpw, ipw, n_hg, n_ig;  // query-major grid (as the forward)
   int* kcount;  // [B*Hkv*Tc] kept items per key block (scoring pass)
   int* pairs;   // [B*Hkv][npair][2] key-block pairs of the dK/dV pass; -1 = none
-  int* segtab;  // [B*Hkv*Tc] segments of each key block's pair
+  int* segtab;  // [B*Hkv*Tc] key block's pair: nseg | side << 4 | first slot << 5
   int npair;    // pair slots per (batch, KV head)
   int* work;    // [B*Hkv][wmax] dK/dV work items: pair | seg << 20 | nseg << 24
   int* wcnt;    // [B*Hkv] work items per (batch, KV head)
@@ -85,17 +96,6 @@ struct BwdParams {
   unsigned long long* counters;
   uint8_t* decisions;
 };
-
-// Causal legal tiles: query block i reaches key blocks 0 .. min(tc - 1,
-// i + cblk), so the decision map stores min(tc, i + cblk + 1) bytes for it;
-// causal_row_start(i) is the number stored for the blocks before i (the
-// lower triangle when nq = nk).
-__host__ __device__ __forceinline__ long long causal_row_start(long long i, long long tc,
-                                                               long long cblk) {
-  const long long istar = tc - cblk - 1 > 0 ? tc - cblk - 1 : 0;  // blocks that reach every key block
-  const long long m = i < istar ? i : istar;
-  return m * (m - 1) / 2 + m * (cblk + 1) + (i - m) * tc;
-}
 
 // Decision byte of tile (i, j) of (batch, query head) bh.
 __device__ __forceinline__ long long dmap_index(const BwdParams& p, int bh, int i, int j) {
@@ -142,6 +142,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
   const int qq = 64 * i + r;
   const bool valid = prow < nprow && qq < p.nq;
   const long long row = bh * p.nq + qq;
+  if (t == 0) *p.status = 0;  // no wait has given up (read by the later passes)
   float acc = 0.f;
   if (valid) {
     const bf16x8 a = *(const bf16x8*)(p.o + row * D + 8 * part);
@@ -185,9 +186,11 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 //     all four of an item's waves are done with it. There is no workgroup
 //     barrier in the loop, and the compute waves issue no copies.
 //   * The copy wave publishes everything it has issued before it waits, so
-//     no wait can be circular. Every wait also has a bound far beyond any
-//     legal schedule; a wait that reached it would raise a workgroup flag that
-//     ends every other wait, so that every wave exits whatever happens.
+//     no wait can be circular. Every wait also has a bound (p.spin polls, by
+//     default far beyond any legal schedule); a wait that reaches it raises a
+//     workgroup flag that ends every other wait, so that every wave exits
+//     whatever happens, and sets the status word, which makes the later
+//     passes write NaN gradients.
 // Decisions go straight to the byte map read by the dK/dV and dQ passes; the
 // kept-item count of every key block goes to the pairing pass.
 template <int D, bool kTest, bool kStats>
@@ -204,7 +207,6 @@ __global__ __launch_bounds__(576, 1) void bwd_score_kernel(BwdParams p) {
   static_assert(OPS * LAG < 64, "vmcnt range");
   constexpr int RQ = 8;                  // ring slots (even: a slot keeps its parity)
   constexpr int NB = 4;                  // key blocks per workgroup
-  constexpr int kSpin = 1 << 22;         // bound on every wait (in sleeps)
 
   __shared__ __attribute__((aligned(16))) char ring[RQ * SQ];
   __shared__ int full[RQ];  // 1 + the item whose data the slot holds
@@ -232,14 +234,17 @@ __global__ __launch_bounds__(576, 1) void bwd_score_kernel(BwdParams p) {
   }
   if (tid == 0) stop = 0;
   lds_barrier();
-  // wait until ready() holds (false only if the bound was reached somewhere)
+  // wait until ready() holds, or give up: after p.spin unsuccessful polls
+  // (at once when p.spin is 0) this wave raises `stop`, and every wait of
+  // the workgroup returns as soon as it sees it
   auto wait_for = [&](auto ready) {
-    for (int g = 0; !ready(); ++g) {
-      if (__hip_atomic_load(&stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) return;
-      if (g >= kSpin) {
+    for (int g = 0;; ++g) {
+      if (g >= p.spin) {
         __hip_atomic_store(&stop, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         return;
       }
+      if (ready()) return;
+      if (__hip_atomic_load(&stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) return;
       __builtin_amdgcn_s_sleep(1);
     }
   };
@@ -394,6 +399,8 @@ __global__ __launch_bounds__(576, 1) void bwd_score_kernel(BwdParams p) {
   // kept items per key block (waves x and x + 4 score block x)
   if (tid < NB && jb0 + tid < p.tc)
     p.kcount[(size_t)bk * p.tc + jb0 + tid] = csum[tid] + csum[tid + 4];
+  // a wait gave up: the decisions may rest on unfinished copies
+  if (tid == 0 && stop) *p.status = 1;
 }
 
 // ----------------------------------------------------------- coarsen ----
@@ -478,13 +485,17 @@ __global__ __launch_bounds__(256) void bwd_dense_map_kernel(uint8_t* dmap, long 
 // retrieval hub) keep nearly the same items, every query block after them,
 // so they are paired with each other in index order; the rest are paired in
 // index order among themselves. Heavy pairs come first in the table, so the
-// longest work is issued first. Each pair is then split into segments, about
-// one per kSegKept items the pair keeps (at most kSegMax), and the
-// (pair, segment) work items are listed in table order for the dK/dV pass.
-// One workgroup per (batch, KV head).
+// longest work is issued first. Each pair is then split into segments (see
+// kSegKept), the (pair, segment) work items are listed in table order for
+// the dK/dV pass, and every key block's entry in the segment table records
+// its pair's segment count, its side of the pair and, for a pair of several
+// segments, the first of the pair's partial-sum slots. One workgroup per
+// (batch, KV head).
 __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdParams p) {
   __shared__ int wsum[4];
   __shared__ int scan[256];
+  __shared__ int sscan[256];
+  __shared__ long long ksum[4];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int bk = blockIdx.x;
   const int* cnt = p.kcount + (size_t)bk * p.tc;
@@ -525,31 +536,50 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdParams p) {
     hrun += wsum[0] + wsum[1] + wsum[2] + wsum[3];
     __syncthreads();
   }
-  // work items, in table order (the barrier above also made the table
-  // visible to the whole workgroup)
+  // segment length from the items all key blocks keep
+  long long kall = 0;
+  for (int j = tid; j < p.tc; j += 256) kall += cnt[j];
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) kall += __shfl_xor(kall, off);
+  if (lane == 0) ksum[w] = kall;
+  __syncthreads();
+  kall = ksum[0] + ksum[1] + ksum[2] + ksum[3];
+  const long long lseg = max((long long)kSegKept, (kall + p.npair - 1) / p.npair);
+  // work items in table order and partial-sum slots (the barrier above also
+  // made the pair table visible to the whole workgroup)
   int* work = p.work + (size_t)bk * p.wmax;
-  int base = 0;
+  int* seg = p.segtab + (size_t)bk * p.tc;
+  int base = 0, sbase = 0;
   for (int x0 = 0; x0 < p.npair; x0 += 256) {
     const int pr = x0 + tid;
-    int nseg = 0;
+    int nseg = 0, jA = -1, jB = -1;
     if (pr < p.npair) {
-      const int jA = pairs[2 * pr], jB = pairs[2 * pr + 1];
+      jA = pairs[2 * pr];
+      jB = pairs[2 * pr + 1];
       if (jA >= 0) {
-        const int kept = cnt[jA] + (jB >= 0 ? cnt[jB] : 0);
-        nseg = min(kSegMax, max(1, (kept + kSegKept - 1) / kSegKept));
+        const long long kept = cnt[jA] + (jB >= 0 ? cnt[jB] : 0);
+        nseg = (int)min((long long)kSegMax, max(1ll, (kept + lseg - 1) / lseg));
       }
     }
+    const int nslot = nseg > 1 ? nseg : 0;
     scan[tid] = nseg;
+    sscan[tid] = nslot;
     __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {  // inclusive prefix sum
+    for (int off = 1; off < 256; off <<= 1) {  // inclusive prefix sums
       const int v = tid >= off ? scan[tid - off] : 0;
+      const int u = tid >= off ? sscan[tid - off] : 0;
       __syncthreads();
       scan[tid] += v;
+      sscan[tid] += u;
       __syncthreads();
     }
     const int first = base + scan[tid] - nseg;
+    const int slot = sbase + sscan[tid] - nslot;  // < 2 npair (see kSegKept)
     for (int sg = 0; sg < nseg; ++sg) work[first + sg] = pr | (sg << 20) | (nseg << 24);
+    if (jA >= 0) seg[jA] = nseg | (0 << 4) | (slot << 5);
+    if (jB >= 0) seg[jB] = nseg | (1 << 4) | (slot << 5);
     base += scan[255];
+    sbase += sscan[255];
     __syncthreads();
   }
   if (tid == 0) p.wcnt[bk] = base;
@@ -624,10 +654,6 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   const int jlo = jB >= 0 ? min(jA, jB) : jA;
   const int i_lo = first_qblock(p, jlo);
   const int n_all = p.group * (p.tr - i_lo);
-  if (seg == 0 && tid < 2 && p.segtab) {
-    const int jx = tid ? jB : jA;
-    if (jx >= 0) p.segtab[(size_t)bk * p.tc + jx] = nseg;
-  }
   const int j = sb ? jB : jA;  // this wave's key block (-1: none)
   const __bf16* kbase = p.k + (size_t)bk * p.nk * D;
   const __bf16* vbase = p.v + (size_t)bk * p.nk * D;
@@ -834,10 +860,12 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   }
   // ---- output: lane holds key 32 kh + l32 of block j, register 4e' + r of
   //      subtile dt = column 32 dt + 8e' + 4hh + r: dK = scale * sum and dV
-  //      directly when the pair has one segment, else fp32 partials ----
+  //      directly when the pair has one segment, else fp32 partials in the
+  //      pair's slots (NaN when a wait of the scoring pass gave up) ----
   if (j < 0) return;
   if (nseg == 1) {
     if (key >= p.nk) return;
+    const float poison = *p.status ? NAN : 1.f;
     __bf16* dkr = p.dk + ((size_t)bk * p.nk + key) * D;
     __bf16* dvr = p.dv + ((size_t)bk * p.nk + key) * D;
 #pragma unroll
@@ -847,15 +875,16 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
         bf16x4 tk, tv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          tk[r] = to_bf16(dkt[d2][4 * e4 + r] * p.scale);
-          tv[r] = to_bf16(dvt[d2][4 * e4 + r]);
+          tk[r] = to_bf16(dkt[d2][4 * e4 + r] * p.scale * poison);
+          tv[r] = to_bf16(dvt[d2][4 * e4 + r] * poison);
         }
         *(bf16x4*)(dkr + 32 * d2 + 8 * e4 + 4 * hh) = tk;
         *(bf16x4*)(dvr + 32 * d2 + 8 * e4 + 4 * hh) = tv;
       }
   } else {
     const int row = 32 * kh + l32;
-    float* pk = p.part + (((size_t)bk * p.tc + j) * kSegMax + seg) * 2 * 64 * D + row * D;
+    const int slot = p.segtab[(size_t)bk * p.tc + j] >> 5;
+    float* pk = p.part + (((size_t)bk * 2 * p.npair + slot + seg) * 2 + sb) * 2 * 64 * D + row * D;
     float* pv = pk + 64 * D;
 #pragma unroll
     for (int d2 = 0; d2 < NDT; ++d2)
@@ -885,13 +914,16 @@ __global__ __launch_bounds__(256) void bwd_kv_finalize_kernel(BwdParams p) {
   const long long bj = e / D / 64;  // bk * Tc + j
   const int j = (int)(bj % p.tc);
   const long long bk = bj / p.tc;
-  const int nseg = p.segtab[bj];
+  const int st = p.segtab[bj];
+  const int nseg = st & 15, side = (st >> 4) & 1, slot = st >> 5;
   const int kk = 64 * j + row;
   if (nseg <= 1 || kk >= p.nk) return;
+  const float poison = *p.status ? NAN : 1.f;
   float ak[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float av[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int sg = 0; sg < nseg; ++sg) {
-    const float* pk = p.part + ((bj * kSegMax + sg) * 2 * 64 + row) * D + col;
+    const float* pk =
+        p.part + (((bk * 2 * p.npair + slot + sg) * 2 + side) * 2 * 64 + row) * D + col;
     const float* pv = pk + 64 * D;
     const float4 k0 = *(const float4*)pk, k1 = *(const float4*)(pk + 4);
     const float4 v0 = *(const float4*)pv, v1 = *(const float4*)(pv + 4);
@@ -903,8 +935,8 @@ __global__ __launch_bounds__(256) void bwd_kv_finalize_kernel(BwdParams p) {
   bf16x8 ok, ov;
 #pragma unroll
   for (int x = 0; x < 8; ++x) {
-    ok[x] = to_bf16(ak[x] * p.scale);
-    ov[x] = to_bf16(av[x]);
+    ok[x] = to_bf16(ak[x] * p.scale * poison);
+    ov[x] = to_bf16(av[x] * poison);
   }
   *(bf16x8*)(p.dk + ((size_t)bk * p.nk + kk) * D + col) = ok;
   *(bf16x8*)(p.dv + ((size_t)bk * p.nk + kk) * D + col) = ov;
@@ -1114,8 +1146,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
     }
   }
 
-  // ---- dQ = scale * acc (bf16); lane holds query column l16, d rows 4g4+r ----
+  // ---- dQ = scale * acc (bf16); lane holds query column l16, d rows 4g4+r
+  //      (NaN when a wait of the scoring pass gave up) ----
   if (valid) {
+    const float sc = *p.status ? NAN : p.scale;
 #pragma unroll
     for (int qs = 0; qs < NQS; ++qs) {
       const int qq = q0 + 16 * qs + l16;
@@ -1124,10 +1158,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) {
         bf16x4 t;
-        t[0] = to_bf16(acc[ds][qs][0] * p.scale);
-        t[1] = to_bf16(acc[ds][qs][1] * p.scale);
-        t[2] = to_bf16(acc[ds][qs][2] * p.scale);
-        t[3] = to_bf16(acc[ds][qs][3] * p.scale);
+        t[0] = to_bf16(acc[ds][qs][0] * sc);
+        t[1] = to_bf16(acc[ds][qs][1] * sc);
+        t[2] = to_bf16(acc[ds][qs][2] * sc);
+        t[3] = to_bf16(acc[ds][qs][3] * sc);
         *(bf16x4*)(row + 16 * ds + 4 * g4) = t;
       }
     }
@@ -1201,20 +1235,6 @@ hipError_t launch_d(const BwdParams& p, bool test, hipStream_t stream) {
 
 }  // namespace
 
-size_t bwd_workspace_bytes(int batch, int heads_q, int heads_kv, int nq, int nk, int head_dim,
-                           int causal) {
-  const size_t tr = (size_t)(nq + 63) / 64, tc = (size_t)(nk + 63) / 64;
-  const size_t rowinfo = (size_t)batch * heads_q * tr * kRowInfo * sizeof(float);
-  const long long off = causal ? (long long)nk - nq : 0;
-  const size_t per_head =
-      causal ? (size_t)causal_row_start((long long)tr, (long long)tc, (63 + off) / 64) : tr * tc;
-  const size_t dmap = (size_t)batch * heads_q * per_head;
-  const size_t part = (size_t)batch * heads_kv * tc * kSegMax * 2 * 64 * head_dim * sizeof(float);
-  const size_t npair = tc / 2 + 1;
-  const size_t tabs = (size_t)batch * heads_kv * (2 * tc + 2 * npair + npair * kSegMax + 1) * sizeof(int);
-  return ((rowinfo + 255) & ~(size_t)255) + ((dmap + 255) & ~(size_t)255) + part + tabs;
-}
-
 hipError_t launch_bwd(const BwdArgs& a, bool test, hipStream_t stream) {
   BwdParams p;
   p.q = (const __bf16*)a.q;
@@ -1242,16 +1262,18 @@ hipError_t launch_bwd(const BwdArgs& a, bool test, hipStream_t stream) {
   p.tc = (a.nk + 63) / 64;
   p.dmap_per_head = p.causal ? causal_row_start(p.tr, p.tc, p.cblk) : (long long)p.tr * p.tc;
   const size_t rowinfo = (size_t)a.batch * a.heads_q * (size_t)p.tr * kRowInfo * sizeof(float);
-  p.rowinfo = (float*)a.workspace;
-  p.dmap = (uint8_t*)a.workspace + ((rowinfo + 255) & ~(size_t)255);
+  p.status = (int*)a.workspace;
+  p.spin = a.spin;
+  p.rowinfo = (float*)((char*)a.workspace + kBwdHeader);
+  p.dmap = (uint8_t*)p.rowinfo + ((rowinfo + 255) & ~(size_t)255);
   const size_t dmap_bytes = (size_t)a.batch * a.heads_q * (size_t)p.dmap_per_head;
   p.part = (float*)(p.dmap + ((dmap_bytes + 255) & ~(size_t)255));
   p.npair = p.tc / 2 + 1;
   const size_t nkb = (size_t)a.batch * a.heads_kv * p.tc;
-  p.kcount = (int*)(p.part + nkb * kSegMax * 2 * 64 * a.head_dim);
+  const size_t nbk = (size_t)a.batch * a.heads_kv;
+  p.kcount = (int*)(p.part + nbk * 2 * p.npair * 2 * 2 * 64 * a.head_dim);
   p.segtab = p.kcount + nkb;
   p.pairs = p.segtab + nkb;
-  const size_t nbk = (size_t)a.batch * a.heads_kv;
   p.wmax = p.npair * kSegMax;
   p.work = p.pairs + nbk * p.npair * 2;
   p.wcnt = p.work + nbk * p.wmax;

@@ -27,7 +27,11 @@
 //     and the exponentials overlap;
 //   * exponentials use a reference maximum that moves only on jumps of more
 //     than 8 (log2 units), which makes the O rescale rare;
-//   * workgroups are issued longest-first (largest query block first).
+//   * workgroups are issued longest-first (largest query block first);
+//   * every wait for a partner's vote is bounded (FwdParams::spin polls): a
+//     wave that reaches the bound raises a workgroup flag that ends every
+//     other wait, and the workgroup then writes NaN for O and LSE, so a
+//     give-up can never pass for a result.
 #include "mala_common.h"
 #include "mala_internal.h"
 
@@ -46,6 +50,7 @@ struct FwdParams {
   int cblk;  // causal: query block i reaches key block i + cblk, cblk = (63 + off) / 64
   float c;         // softmax_scale * log2(e): raw score -> log2 units
   float log2_tau;  // log2(tau); -inf for tau = 0, +inf for tau = inf
+  int spin;        // bound on each wait for a partner wave's vote (polls)
   int group;       // heads_q / heads_kv
   int hpw, ipw;    // heads x query blocks per workgroup, hpw * ipw = 4
   int n_hg, n_ig;  // head groups per KV head, query-block groups
@@ -79,6 +84,8 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   __shared__ int vflags[2][8];  // block decisions, read after the next barrier
   __shared__ int pflags[8];     // row-half ballots, tagged with the tile
   __shared__ int lflags[8];     // 128-key tiles: V of the upper tile requested late
+  __shared__ int fstop;         // a wait for a vote reached its bound
+  __shared__ int spin_lds;      // the bound (p.spin)
 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
@@ -137,6 +144,10 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   // that no wait for them lands inside the pipelined loop
   vmcnt_wait<0>();
   if (tid < 8) pflags[tid] = 0;
+  if (tid == 0) {
+    fstop = 0;
+    spin_lds = p.spin;
+  }
 
   floatx16 oacc[NDT];
 #pragma unroll
@@ -306,17 +317,27 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
   // votes of the waves that decide the tile with it: the other row half of
   // the block and, with 128-row tiles, both halves of the paired block. All
   // of them take this path for the same tiles and nothing between the
-  // barrier and here waits on another wave, so the waits end.
+  // barrier and here waits on another wave, so the waits end. Each wait is
+  // also bounded: after p.spin unsuccessful polls (at once when p.spin is 0)
+  // the wave gives up and raises fstop, which makes the workgroup write NaN
+  // outputs.
   auto exchange = [&](int j, bool mine) {
     const int tag = 2 * (j + 1);
     __hip_atomic_store(&pflags[w], tag | (mine ? 1 : 0), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_WORKGROUP);
     bool any = mine;
     auto take = [&](int x) {
-      int o;
-      do {
+      // poll up to the bound (kept in LDS, so that no register holds it
+      // through the kernel)
+      int o = 0, left = spin_lds;
+      for (; left > 0; --left) {
         o = __hip_atomic_load(&pflags[x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      } while ((o & ~1) != tag);
+        if ((o & ~1) == tag) break;
+      }
+      if (left == 0) {
+        __hip_atomic_store(&fstop, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        o = 0;
+      }
       any = any || (o & 1);
     };
     take(w ^ 1);
@@ -499,7 +520,10 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
     }
     if (w == 0) atomicAdd(&p.counters[3], st_vtiles);
   }
-  // ---- finalisation: O = O / l, LSE = m + log l ----
+  // ---- finalisation: O = O / l, LSE = m + log l (NaN if a wait gave up;
+  //      every wave has passed its last exchange at this barrier) ----
+  lds_barrier();
+  if (fstop) lsum = NAN;
   if (row_ok) {
     const float inv = 1.f / lsum;
     __bf16* orow = p.o + (qrow0 + qq) * D;
@@ -557,6 +581,7 @@ hipError_t launch_fwd(const FwdArgs& a, bool test, hipStream_t stream) {
   p.cblk = (63 + p.off) / 64;
   p.c = a.scale * kLog2e;
   p.log2_tau = a.tau == 0.f ? -INFINITY : log2f(a.tau);
+  p.spin = a.spin;
   p.group = a.heads_q / a.heads_kv;
   const bool bq2 = a.block_q == 128, bk2 = a.block_k == 128;
   if (p.group % 4 == 0 && !bq2) {

@@ -116,7 +116,11 @@ typedef struct {
  * block 0. Each tile is scored; it is skipped when every valid query row with
  * a legal key in it has rowmax - m - log l < log(tau / L_q); otherwise V is
  * loaded and every valid row of the block takes the online-softmax update.
- * Writes O (bf16) and LSE (fp32) only. Works for training and prefill. */
+ * Writes O (bf16) and LSE (fp32) only. Works for training and prefill.
+ * The waves that decide a tile together exchange their votes through LDS
+ * with a bounded wait (MALA_WAIT_BOUND as for mala_bwd); if a wait reaches
+ * its bound, O and LSE of that workgroup's query blocks are written as NaN
+ * (never as a plausible value). */
 int mala_fwd(const mala_shape* shape, const mala_config* cfg, const void* q, const void* k,
              const void* v, void* o, float* lse, const mala_stats* stats, void* stream);
 
@@ -125,16 +129,19 @@ int mala_fwd(const mala_shape* shape, const mala_config* cfg, const void* q, con
 int fullattn_fwd(const mala_shape* shape, const mala_config* cfg, const void* q, const void* k,
                  const void* v, void* o, float* lse, const mala_stats* stats, void* stream);
 
-/* Bytes of device workspace mala_bwd / fullattn_bwd need: fp32 row terms
- * per 64-row query block (z = LSE in log2 units, the test threshold and
- * D = rowsum(O o dO); 1 KiB per block), one decision byte per legal tile
- * (when causal, query block i reaches key blocks 0 .. i + (63 + seqlen_k -
- * seqlen_q) / 64), and fp32 partial dK/dV sums for up to 8
- * segments per 64-key block (8 x 2 x 64 x head_dim x 4 bytes per key block
- * and KV head: 512 KiB at head_dim 128), and int32 tables per (batch, KV
- * head): kept items and segments per key block, the Tc/2 + 1 key-block pairs
- * the dK/dV pass runs and up to 8 work items per pair, and the work count
- * (Tc = key blocks). Returns 0 for an invalid shape or config. */
+/* Bytes of device workspace mala_bwd / fullattn_bwd need: a 256-byte header
+ * (int32 status word, see mala_bwd), fp32 row terms per 64-row query block
+ * (z = LSE in log2 units, the test threshold and D = rowsum(O o dO); 1 KiB
+ * per block), one decision byte per legal tile (when causal, query block i
+ * reaches key blocks 0 .. i + (63 + seqlen_k - seqlen_q) / 64), fp32
+ * partial dK/dV sums for 2 npair segment slots per (batch, KV head), npair
+ * = ceil(seqlen_k / 64) / 2 + 1, each slot holding a pair of 64-key blocks
+ * (2 x 2 x 64 x head_dim x 4 bytes: 128 KiB at head_dim 128; the dK/dV pass
+ * segments long pairs so that all segments of all pairs fit, whatever the
+ * decisions), and int32 tables per (batch, KV head): kept items and the
+ * segment entry per key block, the npair key-block pairs of the dK/dV pass
+ * with up to 8 work items each, and the work count. Returns 0 for an
+ * invalid shape or config. */
 size_t mala_bwd_workspace_bytes(const mala_shape* shape, const mala_config* cfg);
 
 /* MALA backward (Algorithm 2; Eq. 4; the backward part of Appendix A.1).
@@ -147,7 +154,13 @@ size_t mala_bwd_workspace_bytes(const mala_shape* shape, const mala_config* cfg)
  * dK products, and a query-major pass forms dQ over the kept tiles
  * (deterministic: no atomics). o and lse are the forward's outputs. dQ, dK, dV are
  * overwritten (rows without a kept tile get zeros). workspace must hold
- * mala_bwd_workspace_bytes(); its contents on entry are irrelevant. */
+ * mala_bwd_workspace_bytes(); its contents on entry are irrelevant.
+ * Failure signal: the scoring pass's waves wait on one another with a
+ * bound (the environment variable MALA_WAIT_BOUND, read per call, overrides
+ * it for tests; 0 makes every wait give up). If a wait reaches its bound,
+ * every kernel still runs to completion, dQ, dK and dV are written as NaN
+ * everywhere, and the int32 at the start of the workspace reads 1 after the
+ * call (0 otherwise). The status code only reports host-side errors. */
 int mala_bwd(const mala_shape* shape, const mala_config* cfg, const void* q, const void* k,
              const void* v, const void* o, const float* lse, const void* dout, void* dq,
              void* dk, void* dv, void* workspace, size_t workspace_bytes,

@@ -17,6 +17,17 @@ replaced by |a|*|b|).
     moves D_q by at most 2^-7 sum_d |O_qd dO_qd| and dS by P times that, so
     M_D is the dQ / dK sum with dS replaced by P * sum_d |O dO|;
   * V2: sum|X_gpu - X_bf16| / sum|X_bf16| <= 1e-3 (mean relative error);
+  * V1 against fp64 (elementwise): |X_gpu - X_exact| <= 2^-6 (M + |X_exact|
+    + M_D) + 1e-4. It follows from V1: the bf16-operand model itself differs
+    from the exact result by at most 2^-9 M per rounded operand (each term of
+    a product moves by at most 2^-9 of itself, and the terms' magnitudes sum
+    to M) plus 2^-9 |X| for the rounding of the output, and 2^-7 (M + |X| +
+    M_D) + 2^-8 M + 2^-9 |X| <= 2^-6 (M + |X| + M_D). The survey's first
+    reading, |X_gpu - X_exact| <= 2e-2 max(1, |X_exact|), is not a bound the
+    arithmetic gives: where dQ = sum dS K cancels, bf16 rounding of the dS
+    operands leaves an error that scales with M, not with |dQ|. Its value,
+    max |X_gpu - X_exact| / max(1, |X_exact|), is reported beside V2
+    (v1_exact_metric);
   * L2 (fidelity to the fp64 oracle, the relative L2 error the paper uses,
     App. C.3): ||X_gpu - X_exact|| <= 2^-7 (||M|| + ||X_exact|| + ||M_D||)
     (bf16 operand rounding, at most 2^-9 of each term, with a factor 4 of
@@ -40,7 +51,6 @@ import oracle as O
 import workloads as W
 
 DELTA = 2e-3
-V1_TOL = 2e-2
 V2_TOL = 1e-3
 LSE_TOL = 1e-3
 AGREE_MIN = 0.999
@@ -62,6 +72,22 @@ def v1_ok(x, model, mag, mag_d=0.0):
     err = np.abs(x - model)
     bound = 2.0 ** -7 * (mag + np.abs(model) + mag_d) + 1e-4
     return bool((err <= bound).all()), float((err / bound).max()) if err.size else 0.0
+
+
+def v1_exact_ok(x, exact, mag, mag_d=0.0):
+    """Elementwise bound against the exact fp64 result (see the module
+    docstring). Returns (ok, worst ratio of error to bound)."""
+    err = np.abs(x - exact)
+    bound = 2.0 ** -6 * (mag + np.abs(exact) + mag_d) + 1e-4
+    return bool((err <= bound).all()), float((err / bound).max()) if err.size else 0.0
+
+
+def v1_exact_metric(x, exact):
+    """max |x - exact| / max(1, |exact|): the survey's elementwise metric,
+    reported (not asserted)."""
+    if x.size == 0:
+        return 0.0
+    return float((np.abs(x - exact) / np.maximum(1.0, np.abs(exact))).max())
 
 
 def l2_ok(x, exact, mag, mag_d=0.0):
