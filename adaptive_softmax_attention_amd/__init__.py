@@ -71,7 +71,11 @@ class Stats:
 
 EXPORTS = ("mala_fwd", "fullattn_fwd", "mala_bwd_workspace_bytes", "mala_bwd", "fullattn_bwd",
            "mala_decode_workspace_bytes", "mala_decode_default_splits", "mala_decode",
-           "fullattn_decode", "mala_decode_paged", "fullattn_decode_paged", "mala_status_string")
+           "fullattn_decode", "mala_decode_noalloc", "mala_decode_paged", "fullattn_decode_paged",
+           "mala_status_string")
+
+# device-resident scratch of mala_decode_noalloc (bytes per GPU; mala.h)
+DECODE_NOALLOC_MAX_BYTES = 16 << 20
 
 _lib = None
 
@@ -99,6 +103,8 @@ def lib():
         for f in ("mala_decode", "fullattn_decode"):
             getattr(L, f).argtypes = [ps, pc, vp, vp, vp, vp, vp, ctypes.c_int32, vp, sz, pst, vp]
             getattr(L, f).restype = ctypes.c_int
+        L.mala_decode_noalloc.argtypes = [ps, pc, vp, vp, vp, vp, vp, ctypes.c_int32, pst, vp]
+        L.mala_decode_noalloc.restype = ctypes.c_int
         for f in ("mala_decode_paged", "fullattn_decode_paged"):
             getattr(L, f).argtypes = [ps, pc, vp, vp, vp, vp, vp, ctypes.c_int32, vp, vp,
                                       ctypes.c_int32, vp, sz, pst, vp]
@@ -293,6 +299,29 @@ def fullattn_decode(q, k_cache, v_cache, o, lse, num_splits, workspace, *, block
     """Dense split-KV decode from the same kernels (test compiled out)."""
     _decode("fullattn_decode", q, k_cache, v_cache, o, lse, num_splits, workspace, 0.0, block_k,
             softmax_scale, stats, stream)
+
+
+def mala_decode_noalloc(q, k_cache, v_cache, o, lse, num_splits, *, tau=1.0, block_k=64,
+                        softmax_scale=None, stats=None, stream=None):
+    """mala_decode without a workspace: the split partials go to the
+    library's device-resident array (at most DECODE_NOALLOC_MAX_BYTES per
+    GPU). For callers that cannot allocate; overlapping calls on one GPU
+    race."""
+    import torch
+    B, Hq, d = q.shape
+    _check(q, "q", torch.bfloat16, q.shape)
+    _check(k_cache, "k_cache", torch.bfloat16, (B, k_cache.shape[1], k_cache.shape[2], d))
+    _check(v_cache, "v_cache", torch.bfloat16, k_cache.shape)
+    _check(o, "o", torch.bfloat16, q.shape)
+    _check(lse, "lse", torch.float32, (B, Hq))
+    shp = make_shape(q, k_cache, decode=True)
+    cfg = make_config(False, tau, 64, block_k, softmax_scale, d)
+    st = stats._c() if stats is not None else None
+    rc = lib().mala_decode_noalloc(ctypes.byref(shp), ctypes.byref(cfg), _ptr(q), _ptr(k_cache),
+                                   _ptr(v_cache), _ptr(o), _ptr(lse), int(num_splits),
+                                   ctypes.byref(st) if st is not None else None, _stream(stream))
+    if rc != MALA_OK:
+        raise MalaError(rc, "mala_decode_noalloc")
 
 
 def _decode_paged(name, q, k_pages, v_pages, block_table, cache_lens, max_len, o, lse,

@@ -10,6 +10,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include <hip/hip_runtime.h>
 
@@ -84,6 +85,36 @@ int wait_bound() {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ---- device-resident scratch of mala_decode_noalloc -------------------------
+// The split partials (m, l, u) of the allocation-free decode entry point live
+// in this file-scope device array: each GPU the library runs on holds its own
+// copy, at its own address, until the process ends. Host code never uses the
+// array's name as an address (on the host it names a stand-in, not device
+// memory); the address is looked up once per device with
+// hipGetSymbolAddress, with that device current, and kept.
+constexpr size_t kDecodeScratchBytes = 16u << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __attribute__((aligned(256))) char scratch[kDecodeScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (looked up on the first call on
+// that device).
+int decode_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MALA_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+      return MALA_ERR_DEVICE;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MALA_OK;
+}
 
 // The kernels move bf16 rows in 16-byte vectors and the workspace in float4
 // words; lse, tables and lengths are read as 4-byte words, counters as
@@ -195,12 +226,14 @@ int bwd_common(const mala_shape* shape, const mala_config* cfg, const void* q, c
   return launch_status(mala::launch_bwd(a, test, (hipStream_t)stream));
 }
 
+// use_scratch: the partials go to the device-resident scratch array instead
+// of a caller workspace (workspace / workspace_bytes are then ignored).
 int decode_common(const mala_shape* shape, const mala_config* cfg, const void* q,
                   const void* k_cache, const void* v_cache, void* o, float* lse,
                   int32_t num_splits, void* workspace, size_t workspace_bytes,
                   const mala_stats* stats, void* stream, bool test,
                   const int32_t* block_table = nullptr, const int32_t* cache_lens = nullptr,
-                  int32_t num_pages = 0) {
+                  int32_t num_pages = 0, bool use_scratch = false) {
   int st = check_shape(shape);
   if (st) return st;
   st = check_config(cfg, test);
@@ -216,11 +249,19 @@ int decode_common(const mala_shape* shape, const mala_config* cfg, const void* q
   const int64_t tc = (shape->seqlen_k + cfg->block_k - 1) / cfg->block_k;
   if (num_splits > tc) return MALA_ERR_INVALID_ARG;  // every split owns >= 1 decision tile
   const size_t need = mala_decode_workspace_bytes(shape, num_splits);
-  if (!workspace || workspace_bytes < need) return MALA_ERR_WORKSPACE;
-  if (!aligned(workspace, 16)) return MALA_ERR_INVALID_ARG;
+  if (use_scratch) {
+    if (need > kDecodeScratchBytes) return MALA_ERR_WORKSPACE;
+  } else {
+    if (!workspace || workspace_bytes < need) return MALA_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return MALA_ERR_INVALID_ARG;
+  }
   if ((int64_t)shape->batch * shape->heads_kv * num_splits > kMaxGrid) return MALA_ERR_UNSUPPORTED;
   st = check_device();
   if (st) return st;
+  if (use_scratch) {
+    st = decode_scratch(&workspace);
+    if (st) return st;
+  }
   mala::DecodeArgs a;
   a.q = q;
   a.k = k_cache;
@@ -318,6 +359,13 @@ int fullattn_decode(const mala_shape* shape, const mala_config* cfg, const void*
                     const mala_stats* stats, void* stream) {
   return decode_common(shape, cfg, q, k_cache, v_cache, o, lse, num_splits, workspace,
                        workspace_bytes, stats, stream, false);
+}
+
+int mala_decode_noalloc(const mala_shape* shape, const mala_config* cfg, const void* q,
+                        const void* k_cache, const void* v_cache, void* o, float* lse,
+                        int32_t num_splits, const mala_stats* stats, void* stream) {
+  return decode_common(shape, cfg, q, k_cache, v_cache, o, lse, num_splits, nullptr, 0, stats,
+                       stream, true, nullptr, nullptr, 0, true);
 }
 
 int mala_decode_paged(const mala_shape* shape, const mala_config* cfg, const void* q,

@@ -203,6 +203,22 @@ int fullattn_decode(const mala_shape* shape, const mala_config* cfg, const void*
                     int32_t num_splits, void* workspace, size_t workspace_bytes,
                     const mala_stats* stats, void* stream);
 
+/* mala_decode without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation). Same arguments, kernels and results as mala_decode;
+ * the split partials go to a device-resident array of the library instead
+ * of a caller workspace: at most 16 MiB (16 << 20 bytes) per GPU, held until
+ * the process ends. A call needing more (mala_decode_workspace_bytes() >
+ * 16 MiB) returns MALA_ERR_WORKSPACE before any device call. The call
+ * allocates nothing (the array's device address is looked up once per
+ * device, on the first call with that device current). Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (on different
+ * streams, or from different host threads) race and must be serialised by
+ * the caller. */
+int mala_decode_noalloc(const mala_shape* shape, const mala_config* cfg, const void* q,
+                        const void* k_cache, const void* v_cache, void* o, float* lse,
+                        int32_t num_splits, const mala_stats* stats, void* stream);
+
 /* Split-KV decode over a paged cache of variable-length sequences (the MALA
  * paper's Sec. 2.4 and the decoding part of its Appendix A.1; the serving
  * layout is this library's). Sequence b holds cache_lens[b] keys (1 <= cache_lens[b] <=

@@ -110,6 +110,14 @@ int main(void) {
   EXPECT(fullattn_decode_paged(&d, &c, A, A, A, (const int32_t*)A, (const int32_t*)A, 10, A,
                                (float*)A, S, A, dw, NULL, NULL), MALA_ERR_DEVICE);
   EXPECT(mala_decode_workspace_bytes(&d, 0) == 0, 1);
+  /* the allocation-free decode: its scratch holds at most 16 MiB */
+  EXPECT(mala_decode_noalloc(&d, &c, A, A, A, A, (float*)A, S, NULL, NULL), MALA_ERR_DEVICE);
+  mala_shape big = {64, 64, 8, 1, 131072, 128};
+  EXPECT(mala_decode_noalloc(&big, &c, A, A, A, A, (float*)A, 16, NULL, NULL),
+         MALA_ERR_WORKSPACE);
+  EXPECT(mala_decode_noalloc(&d, &c, NULL, A, A, A, (float*)A, S, NULL, NULL),
+         MALA_ERR_INVALID_ARG);
+  EXPECT(mala_decode_noalloc(&d, &c, A, A, A, A, (float*)A, 0, NULL, NULL), MALA_ERR_INVALID_ARG);
   for (int x = -3; x < 12; ++x) EXPECT(mala_status_string(x) != NULL, 1);
 
   /* seeded sweep: random and extreme sizes; every status must be a code */
@@ -132,8 +140,9 @@ int main(void) {
     const int codes[] = {fwd(&r, &g, A), bwd(&r, &g, A, wb ? wb : 1),
                          dec(&r, &g, sp, A, wd ? wd : 1),
                          fullattn_bwd(&r, &g, A, A, A, A, (const float*)A, A, A, A, A, A, wb, NULL,
-                                      NULL)};
-    for (int x = 0; x < 4; ++x)
+                                      NULL),
+                         mala_decode_noalloc(&r, &g, A, A, A, A, (float*)A, sp, NULL, NULL)};
+    for (int x = 0; x < 5; ++x)
       if (codes[x] < MALA_OK || codes[x] > MALA_ERR_LAUNCH) {
         fprintf(stderr, "status %d out of range\n", codes[x]);
         ++fails;

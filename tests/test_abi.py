@@ -26,7 +26,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     L = m.lib()
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(m.EXPORTS)
