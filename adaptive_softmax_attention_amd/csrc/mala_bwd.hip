@@ -53,11 +53,13 @@ namespace {
 // segments' fp32 partial sums are added in a fixed order by the finalize
 // kernel (deterministic, no atomics). A pair keeping `kept` items gets
 // min(kSegMax, ceil(kept / Lseg)) segments with Lseg = max(kSegKept,
-// ceil(K / npair)), K = the items all key blocks of the (batch, KV head)
+// ceil(K / (2 npair))), K = the items all key blocks of the (batch, KV head)
 // keep. A pair with more than one segment keeps more than Lseg items, so its
 // segment count is below 2 kept / Lseg and all such pairs together hold
-// fewer than 2 K / Lseg <= 2 npair segments: the partials need 2 npair
-// slots per (batch, KV head), whatever the decisions.
+// fewer than 2 K / Lseg <= 4 npair segments: the partials need kSlotsPerPair
+// = 4 slots per pair, whatever the decisions. (Measured at 128K: 2 slots per
+// pair, Lseg twice as long, made the dK/dV pass 1.4 ms slower; 8 or 16 gain
+// nothing over 4.)
 constexpr int kSegKept = 512;
 
 struct BwdParams {
@@ -74,7 +76,7 @@ struct BwdParams {
   int spin;        // bound on every wait of the scoring pass (polls)
   float* rowinfo;  // [B*Hq*Tr][kRowInfo]
   uint8_t* dmap;   // backward decisions, see dmap_index()
-  float* part;     // [B*Hkv][2 npair slots][2 blocks][2][64][D] fp32 partial dK, dV
+  float* part;     // [B*Hkv][kSlotsPerPair npair][2 blocks][2][64][D] fp32 partial dK, dV
   int batch, heads_q, heads_kv, nq, nk, group;
   int causal;
   int off;   // causal: query q sits at key position q + off (off = nk - nq >= 0)
@@ -544,7 +546,8 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdParams p) {
   if (lane == 0) ksum[w] = kall;
   __syncthreads();
   kall = ksum[0] + ksum[1] + ksum[2] + ksum[3];
-  const long long lseg = max((long long)kSegKept, (kall + p.npair - 1) / p.npair);
+  const long long lseg = max((long long)kSegKept, (2 * kall + (long long)kSlotsPerPair * p.npair - 1) /
+                                                        ((long long)kSlotsPerPair * p.npair));
   // work items in table order and partial-sum slots (the barrier above also
   // made the pair table visible to the whole workgroup)
   int* work = p.work + (size_t)bk * p.wmax;
@@ -574,7 +577,7 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(BwdParams p) {
       __syncthreads();
     }
     const int first = base + scan[tid] - nseg;
-    const int slot = sbase + sscan[tid] - nslot;  // < 2 npair (see kSegKept)
+    const int slot = sbase + sscan[tid] - nslot;  // < kSlotsPerPair npair (see kSegKept)
     for (int sg = 0; sg < nseg; ++sg) work[first + sg] = pr | (sg << 20) | (nseg << 24);
     if (jA >= 0) seg[jA] = nseg | (0 << 4) | (slot << 5);
     if (jB >= 0) seg[jB] = nseg | (1 << 4) | (slot << 5);
@@ -884,7 +887,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   } else {
     const int row = 32 * kh + l32;
     const int slot = p.segtab[(size_t)bk * p.tc + j] >> 5;
-    float* pk = p.part + (((size_t)bk * 2 * p.npair + slot + seg) * 2 + sb) * 2 * 64 * D + row * D;
+    float* pk = p.part + (((size_t)bk * kSlotsPerPair * p.npair + slot + seg) * 2 + sb) * 2 * 64 * D + row * D;
     float* pv = pk + 64 * D;
 #pragma unroll
     for (int d2 = 0; d2 < NDT; ++d2)
@@ -923,7 +926,7 @@ __global__ __launch_bounds__(256) void bwd_kv_finalize_kernel(BwdParams p) {
   float av[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int sg = 0; sg < nseg; ++sg) {
     const float* pk =
-        p.part + (((bk * 2 * p.npair + slot + sg) * 2 + side) * 2 * 64 + row) * D + col;
+        p.part + (((bk * kSlotsPerPair * p.npair + slot + sg) * 2 + side) * 2 * 64 + row) * D + col;
     const float* pv = pk + 64 * D;
     const float4 k0 = *(const float4*)pk, k1 = *(const float4*)(pk + 4);
     const float4 v0 = *(const float4*)pv, v1 = *(const float4*)(pv + 4);
@@ -1271,7 +1274,7 @@ hipError_t launch_bwd(const BwdArgs& a, bool test, hipStream_t stream) {
   p.npair = p.tc / 2 + 1;
   const size_t nkb = (size_t)a.batch * a.heads_kv * p.tc;
   const size_t nbk = (size_t)a.batch * a.heads_kv;
-  p.kcount = (int*)(p.part + nbk * 2 * p.npair * 2 * 2 * 64 * a.head_dim);
+  p.kcount = (int*)(p.part + nbk * kSlotsPerPair * p.npair * 2 * 2 * 64 * a.head_dim);
   p.segtab = p.kcount + nkb;
   p.pairs = p.segtab + nkb;
   p.wmax = p.npair * kSegMax;

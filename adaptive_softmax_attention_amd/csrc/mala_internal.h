@@ -75,6 +75,7 @@ hipError_t launch_decode(const DecodeArgs& a, bool test, hipStream_t stream);
 constexpr int kRowInfo = 256;       // floats of row terms per 64-row block
 constexpr size_t kBwdHeader = 256;  // bytes before the row terms: the int32 status word
 constexpr int kSegMax = 8;          // dK/dV segments per pair of key blocks, at most
+constexpr int kSlotsPerPair = 4;    // fp32 partial-sum slots per pair of key blocks
 
 // Causal legal tiles: query block i reaches key blocks 0 .. min(tc - 1,
 // i + cblk), so the decision map stores min(tc, i + cblk + 1) bytes for it;
@@ -87,7 +88,7 @@ __host__ __device__ inline long long causal_row_start(long long i, long long tc,
 }
 
 // [header][row terms, B*Hq*Tr blocks][decision map][partial dK/dV: B*Hkv x
-// 2 npair slots x 2 blocks x (dK, dV) x 64 x d fp32][int32 tables: kept items
+// kSlotsPerPair npair slots x 2 blocks x (dK, dV) x 64 x d fp32][int32 tables: kept items
 // and segment entry per key block, npair pairs, npair * kSegMax work items,
 // work count], with npair = Tc / 2 + 1.
 inline size_t bwd_workspace_bytes(int batch, int heads_q, int heads_kv, int nq, int nk,
@@ -99,7 +100,8 @@ inline size_t bwd_workspace_bytes(int batch, int heads_q, int heads_kv, int nq, 
       causal ? (size_t)causal_row_start((long long)tr, (long long)tc, (63 + off) / 64) : tr * tc;
   const size_t dmap = (size_t)batch * heads_q * per_head;
   const size_t npair = tc / 2 + 1;
-  const size_t part = (size_t)batch * heads_kv * 2 * npair * 2 * 2 * 64 * head_dim * sizeof(float);
+  const size_t part =
+      (size_t)batch * heads_kv * kSlotsPerPair * npair * 2 * 2 * 64 * head_dim * sizeof(float);
   const size_t tabs =
       (size_t)batch * heads_kv * (2 * tc + 2 * npair + npair * kSegMax + 1) * sizeof(int);
   return kBwdHeader + ((rowinfo + 255) & ~(size_t)255) + ((dmap + 255) & ~(size_t)255) + part +

@@ -134,7 +134,7 @@ int fullattn_fwd(const mala_shape* shape, const mala_config* cfg, const void* q,
  * (z = LSE in log2 units, the test threshold and D = rowsum(O o dO); 1 KiB
  * per block), one decision byte per legal tile (when causal, query block i
  * reaches key blocks 0 .. i + (63 + seqlen_k - seqlen_q) / 64), fp32
- * partial dK/dV sums for 2 npair segment slots per (batch, KV head), npair
+ * partial dK/dV sums for 4 npair segment slots per (batch, KV head), npair
  * = ceil(seqlen_k / 64) / 2 + 1, each slot holding a pair of 64-key blocks
  * (2 x 2 x 64 x head_dim x 4 bytes: 128 KiB at head_dim 128; the dK/dV pass
  * segments long pairs so that all segments of all pairs fit, whatever the

@@ -32,7 +32,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "mala_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# MALA_ORACLE_LIB names another build of mala_oracle.c (the mutation test
+# loads deliberately broken builds through it); default: the in-tree build
+_LIB = os.environ.get("MALA_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 # rounding flags (mirrors the #defines in mala_oracle.c)
 ROUND_P_FWD = 1

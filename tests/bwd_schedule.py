@@ -9,7 +9,7 @@ maximum of 8 segments, whose finalize adds 8 partials):
   * kept[j]: the (query head, query block) items that keep key block j;
   * heavy blocks: 4 kept[j] >= the items with a legal tile in block j;
     heavy blocks are paired in index order, then the light ones;
-  * K = sum of kept[j], npair = Tc // 2 + 1, Lseg = max(512, ceil(K / npair));
+  * K = sum of kept[j], npair = Tc // 2 + 1, Lseg = max(512, ceil(2 K / (4 npair)));
     a pair keeping `kept` items gets min(8, max(1, ceil(kept / Lseg)))
     segments.
 """
@@ -17,6 +17,7 @@ import numpy as np
 
 SEG_KEPT = 512
 SEG_MAX = 8
+SLOTS_PER_PAIR = 4
 
 
 def pairs_and_segments(bdec, heads_kv, nq, nk, causal=True):
@@ -44,7 +45,7 @@ def pairs_and_segments(bdec, heads_kv, nq, nk, causal=True):
             for x, j in enumerate(lt):
                 table[2 * ph + x] = j
             K = int(kept.sum())
-            lseg = max(SEG_KEPT, -(-K // npair))
+            lseg = max(SEG_KEPT, -(-2 * K // (SLOTS_PER_PAIR * npair)))
             rows = []
             for p in range(npair):
                 jA, jB = table[2 * p], table[2 * p + 1]
