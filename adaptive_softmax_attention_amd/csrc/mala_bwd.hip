@@ -226,9 +226,9 @@ __global__ __launch_bounds__(576, 1) void bwd_score_kernel(BwdParams p) {
   const int b = bk / p.heads_kv, kvh = bk % p.heads_kv;
   const int jb0 = NB * G4;
   const int i_lo = first_qblock(p, jb0);
+  // item it is (group head it % group, query block tr - 1 - it / group); both
+  // sides walk the items in order and step these indices instead of dividing
   const int n_items = p.group * (p.tr - i_lo);
-  auto item_i = [&](int it) { return p.tr - 1 - it / p.group; };
-  auto item_h = [&](int it) { return kvh * p.group + it % p.group; };
 
   if (tid < RQ) {
     full[tid] = 0;
@@ -253,11 +253,12 @@ __global__ __launch_bounds__(576, 1) void bwd_score_kernel(BwdParams p) {
 
   if (w == NC) {
     // ======== copy wave ========
-    // copies of item it: row-major tile, chunks XOR-swizzled per row as the
-    // 32-row operand reads expect (rows past the end re-read the last row),
-    // then the 64 thresholds
-    auto fetch = [&](int it, char* slot) {
-      const int h = item_h(it), i = item_i(it);
+    // copies of the next item: row-major tile, chunks XOR-swizzled per row as
+    // the 32-row operand reads expect (rows past the end re-read the last
+    // row), then the 64 thresholds
+    int fi = p.tr - 1, fh = 0;  // query block and group head of the next item fetched
+    auto fetch = [&](char* slot) {
+      const int h = kvh * p.group + fh, i = fi;
       const __bf16* rows0 = p.q + ((size_t)(b * p.heads_q + h) * p.nq + (size_t)64 * i) * D;
       const int last = p.nq - 1 - 64 * i;  // last row inside the queries
 #pragma unroll
@@ -289,7 +290,11 @@ __global__ __launch_bounds__(576, 1) void bwd_score_kernel(BwdParams p) {
           });
         }
       }
-      fetch(nf, ring + (nf % RQ) * SQ);
+      fetch(ring + (nf % RQ) * SQ);
+      if (++fh == p.group) {
+        fh = 0;
+        --fi;
+      }
       if (nf + 1 - marked > LAG) {  // keep LAG items in flight, publish the older ones
         vmcnt_wait<OPS * LAG>();
         while (marked <= nf - LAG) publish(marked++);
@@ -316,13 +321,15 @@ __global__ __launch_bounds__(576, 1) void bwd_score_kernel(BwdParams p) {
     }
     int kept = 0;
     unsigned long long st_legal = 0, st_kept = 0, st_slots = 0;  // instrumentation
+    // query block and group head of item k, advanced by two items per step
+    int ci = p.tr - 1 - par / p.group, ch = par % p.group;
     for (int k = par; k < n_items; k += 2) {
       const int slot = k % RQ;
       wait_for([&] {
         return __hip_atomic_load(&full[slot], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) ==
                k + 1;
       });
-      const int i = item_i(k);
+      const int i = ci;
       if (live && reaches(p, i, jw)) {
         const char* qt = ring + slot * SQ;
         const float* wr = (const float*)(qt + TB);
@@ -373,7 +380,7 @@ __global__ __launch_bounds__(576, 1) void bwd_score_kernel(BwdParams p) {
         const bool want = kTest ? wave_any(hit) : true;
         kept += want ? 1 : 0;
         if (lane == 0) {
-          const int bh = b * p.heads_q + item_h(k);
+          const int bh = b * p.heads_q + kvh * p.group + ch;
           p.dmap[dmap_index(p, bh, i, jw)] = want ? 1 : 0;
           if (kStats) {
             ++st_legal;
@@ -389,6 +396,11 @@ __global__ __launch_bounds__(576, 1) void bwd_score_kernel(BwdParams p) {
       // products consumed them, and LDS operations of a wave complete in order)
       if (lane == 0)
         __hip_atomic_fetch_add(&done[slot], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      ch += 2;
+      while (ch >= p.group) {
+        ch -= p.group;
+        --ci;
+      }
     }
     if (lane == 0) csum[w] = kept;
     if (kStats && lane == 0 && p.counters) {

@@ -81,7 +81,8 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
 
   __shared__ __attribute__((aligned(16))) __bf16 k_ring[RK][64 * D];
   __shared__ __attribute__((aligned(16))) __bf16 v_ring[RV][64 * D];
-  __shared__ int vflags[2][8];  // block decisions, read after the next barrier
+  // block decisions, a byte per wave, read as one word after the next barrier
+  __shared__ __attribute__((aligned(8))) uint8_t vflags[2][8];
   __shared__ int pflags[8];     // row-half ballots, tagged with the tile
   __shared__ int lflags[8];     // 128-key tiles: V of the upper tile requested late
   __shared__ int fstop;         // a wait for a vote reached its bound
@@ -362,9 +363,7 @@ __global__ __launch_bounds__(512, 1) void fwd_kernel(FwdParams p) {
     const int jn = j + 1;
     int any1 = 0;
     if (jn >= 0 && jn <= jtop) {
-      const int* f = vflags[jn & 1];
-#pragma unroll
-      for (int x = 0; x < 8; ++x) any1 |= f[x];
+      any1 = *(const uint64_t*)vflags[jn & 1] != 0;
       if constexpr (!(kBQ2 || kBK2)) {
         if (kStats && valid && jn <= jmax && half == 0 && lane == 0) {
           ++st_legal;
