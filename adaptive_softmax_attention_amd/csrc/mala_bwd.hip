@@ -477,7 +477,7 @@ __global__ __launch_bounds__(256) void bwd_coarsen_kernel(BwdParams p) {
     atomicAdd(&st[2], s_slots);
   }
   __syncthreads();
-  if (threadIdx.x < j1 - j0) p.kcount[(size_t)bk * p.tc + j0 + threadIdx.x] = cnt[threadIdx.x];
+  if ((int)threadIdx.x < j1 - j0) p.kcount[(size_t)bk * p.tc + j0 + threadIdx.x] = cnt[threadIdx.x];
   if (kStats && threadIdx.x < 3 && p.counters) atomicAdd(&p.counters[threadIdx.x], st[threadIdx.x]);
 }
 
