@@ -101,7 +101,10 @@ __device__ __forceinline__ __bf16 to_bf16(float x) { return static_cast<__bf16>(
 // read, since it cannot tell ring slots apart) nor counts it, which only
 // strengthens the waits it emits for its own loads. All ordering between the
 // copies and the LDS reads of their data is explicit: vmcnt_wait followed by
-// lds_barrier.
+// lds_barrier. The compiler treats M0 as a reserved register and does not
+// honour it as a clobber of inline assembly; the copies are safe because no
+// instruction the compiler generates in these kernels uses M0 (the generated
+// assembly is checked by tests/test_isa_checks.py).
 __device__ __forceinline__ void async_copy16(const void* gsrc, void* lds_base) {
   // the LDS base is wave-uniform (M0); make that explicit to the compiler
   const uint32_t lds = __builtin_amdgcn_readfirstlane(
