@@ -63,6 +63,13 @@
 #define ORC_ABS_D 32       /* backward sensitivity to D: dS replaced by
                               P * sum_d |O||dO| in the dQ / dK sums (|K|, |Q|
                               operands), dV gets no term (it has no D) */
+#define ORC_LAZY_REF 64    /* forward model only: the exponentials of a retained
+                              tile are taken against a reference maximum that
+                              moves only when a tile's row maximum exceeds it by
+                              more than 8 log2 units (P <= 2^8), as the kernel
+                              forms them. In exact arithmetic m + log l, and so
+                              the test and the result, are the same for either
+                              reference; what changes is where P~ is rounded */
 
 typedef struct {
   int32_t batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim;
@@ -307,7 +314,9 @@ static void online_block(const orc_problem* p, const double* q, int64_t q_stride
     if (!retain) continue; /* m, l, O unchanged */
     /* retained tile: online-softmax update of every valid row */
     for (int64_t r = 0; r < nrows; ++r) {
-      const double m_new = mt[r] > m[r] ? mt[r] : m[r];
+      double m_new = mt[r] > m[r] ? mt[r] : m[r];
+      if (p->round_flags & ORC_LAZY_REF) /* 8 log2 units = 8 ln 2 nats */
+        m_new = mt[r] > m[r] + 8.0 * 0.69314718055994530942 ? mt[r] : m[r];
       if (m_new == -INFINITY) continue;
       const double alpha = (m[r] == -INFINITY) ? 0.0 : exp(m[r] - m_new);
       double rowsum = 0.0;

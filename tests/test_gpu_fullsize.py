@@ -163,7 +163,7 @@ def check_fullsize(inp, tau, sel_q, say, label, sample_blocks, kv_per_group=2):
         f"max|dO|/max(1,|O|) {v1_exact_metric(go, fex['o']):.2e}")
     # strict checks on sampled blocks (the oracle's exact magnitudes)
     sb = [(b, h, i) for (b, h, i) in sample_blocks]
-    fbf = O.mala_fwd(q, k, v, tau, round_flags=O.BF16_FWD, force=fex["dec"], sel=sb)
+    fbf = O.mala_fwd(q, k, v, tau, round_flags=O.BF16_FWD | O.LAZY_REF, force=fex["dec"], sel=sb)
     fmag = O.mala_fwd(q, k, v, tau, round_flags=O.BF16_FWD | O.ABS, force=fex["dec"], sel=sb)
     rows = np.zeros((B, Hq, N), dtype=bool)
     for (b, h, i) in sb:

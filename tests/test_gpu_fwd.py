@@ -75,8 +75,9 @@ def compare_fwd(inp, tau, causal=True, sel=None, label="", bq=64, bk=64):
         assert (dec[~legal] == -1).all()
     agree = check_decisions(dec, free, legal)
     ex, flipped = settle_fwd_branch(lambda f: run(f), dec, legal, free=free)
-    # the bf16-operand model follows the exact oracle's settled decisions
-    bf = run(ex["dec"].copy(), O.BF16_FWD)
+    # the bf16-operand model follows the exact oracle's settled decisions and
+    # rounds P~ where the kernel does (against its lazy reference maximum)
+    bf = run(ex["dec"].copy(), O.BF16_FWD | O.LAZY_REF)
     mag = run(ex["dec"].copy(), O.BF16_FWD | O.ABS)
     rows = _rows(sel, q.shape)
     ok, worst = v1_ok(go[rows], bf["o"][rows], mag["o"][rows])

@@ -468,6 +468,34 @@ def test_bf16_operand_mode_is_close_to_exact():
     assert np.abs(r["lse"] - e["lse"]).max() < 1e-5
 
 
+def test_lazy_reference_changes_where_p_is_rounded_not_the_result():
+    """The forward model's lazy reference maximum (the kernel's: it moves only
+    on jumps of more than 8 log2 units) leaves the exact result unchanged: the
+    online softmax is invariant to its reference (Sec. 2.2, m + log l), so
+    without rounding O, LSE and every decision match the plain oracle. With
+    bf16 P~ it rounds at other points than the plain model (P~ up to 2^8), and
+    both stay within bf16 error of exact."""
+    q, k, v, do = _gen_small(N=300, Hq=2, Hkv=1, d=32, planted=6, seed=11)
+    for tau in (0.25, 1.0, 4.0):
+        e = O.mala_fwd(q, k, v, tau, True, 32, 32)
+        z = O.mala_fwd(q, k, v, tau, True, 32, 32, round_flags=O.LAZY_REF)
+        legal = e["dec"] >= 0
+        same = z["dec"] == e["dec"]
+        # a decision may differ only on a tile at the threshold to rounding
+        assert (same | (np.abs(e["margin"]) < 1e-9)).all()
+        assert same[legal].mean() > 0.99
+        if same.all():
+            assert np.abs(z["o"] - e["o"]).max() < 1e-12
+            assert np.abs(z["lse"] - e["lse"]).max() < 1e-12
+    e = O.mala_fwd(q, k, v, 1.0, True, 32, 32)
+    a = O.mala_fwd(q, k, v, 1.0, True, 32, 32, round_flags=O.BF16_FWD, force=e["dec"])
+    b = O.mala_fwd(q, k, v, 1.0, True, 32, 32, round_flags=O.BF16_FWD | O.LAZY_REF,
+                   force=e["dec"])
+    assert np.abs(b["o"] - a["o"]).max() > 0          # other rounding points
+    assert np.abs(b["o"] - e["o"]).max() < 2e-2       # both within bf16 error
+    assert np.abs(b["lse"] - e["lse"]).max() < 1e-5
+
+
 # ------------------------------------------------------- magnitude mode ----
 
 def test_magnitude_mode_bounds_and_matches_twin():
