@@ -1,7 +1,8 @@
 """Seeded random sweep of small problems over the whole parameter space
 (test code): forward, backward and split-KV decode against the oracle, 32
-cases each, and paged variable-length decode, 16 cases; every case is drawn
-from its own seed so that any one reruns alone.
+cases each, paged variable-length decode, 16 cases, and forward and backward
+at 1K-4.5K keys, 6 cases each; every case is drawn from its own seed so that
+any one reruns alone.
 
 A case draws the batch (1-2), the KV heads (1-2) and the group size (1, 2,
 3, 4 or 8), the head dimension (64 or 128), the lengths (1-900 keys; causal
@@ -143,3 +144,35 @@ def test_random_decode_paged(case):
         legal_total += int(legal.sum())
         kept_total += int((gd == 1).sum())
     assert cnt[0] == legal_total and cnt[1] == kept_total
+
+
+def _draw_medium(seed):
+    """A longer problem (1K-4.5K keys, ragged): more key blocks per pair and
+    longer pipelines, still seconds for the oracle."""
+    c = _draw(seed)
+    r = np.random.default_rng(seed + 7)
+    c["Nk"] = int(r.integers(1000, 4501))
+    c["Nq"] = c["Nk"] if (not c["causal"] or r.integers(0, 2)) else int(r.integers(1, c["Nk"] + 1))
+    if not c["causal"]:
+        c["Nq"] = int(r.integers(1000, 4501))
+    c["B"] = 1
+    c["planted"] = int(r.choice([8, 32]))
+    return c
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_random_medium_forward(case):
+    seed = 75000 + case
+    c = _draw_medium(seed)
+    print(f"[random medium fwd] seed {seed} {c}", flush=True)
+    compare_fwd(_prefill(seed, c, False), c["tau"], causal=c["causal"], label=f"rmed{case}",
+                bq=c["bq"], bk=c["bk"])
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_random_medium_backward(case):
+    seed = 76000 + case
+    c = _draw_medium(seed)
+    print(f"[random medium bwd] seed {seed} {c}", flush=True)
+    compare_bwd(_prefill(seed, c, True), c["tau"], causal=c["causal"], label=f"rmed{case}",
+                bq=c["bq"], bk=c["bk"])
