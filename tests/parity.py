@@ -22,8 +22,8 @@ replaced by |a|*|b|).
     from the exact result by at most 2^-9 M per rounded operand (each term of
     a product moves by at most 2^-9 of itself, and the terms' magnitudes sum
     to M) plus 2^-9 |X| for the rounding of the output, and 2^-7 (M + |X| +
-    M_D) + 2^-8 M + 2^-9 |X| <= 2^-6 (M + |X| + M_D). The survey's first
-    reading, |X_gpu - X_exact| <= 2e-2 max(1, |X_exact|), is not a bound the
+    M_D) + 2^-8 M + 2^-9 |X| <= 2^-6 (M + |X| + M_D). The plain elementwise
+    bound |X_gpu - X_exact| <= 2e-2 max(1, |X_exact|) is not a bound the
     arithmetic gives: where dQ = sum dS K cancels, bf16 rounding of the dS
     operands leaves an error that scales with M, not with |dQ|. Its value,
     max |X_gpu - X_exact| / max(1, |X_exact|), is reported beside V2
@@ -83,7 +83,7 @@ def v1_exact_ok(x, exact, mag, mag_d=0.0):
 
 
 def v1_exact_metric(x, exact):
-    """max |x - exact| / max(1, |exact|): the survey's elementwise metric,
+    """max |x - exact| / max(1, |exact|): the plain elementwise metric,
     reported (not asserted)."""
     if x.size == 0:
         return 0.0

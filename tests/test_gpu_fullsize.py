@@ -45,16 +45,16 @@ pytestmark = pytest.mark.gpu
 @pytest.fixture
 def say(capsys):
     """Progress lines that reach the terminal while a long oracle run is in
-    progress (and a progress file when a gpurun_out folder exists)."""
-    root = os.environ.get("GRAFT_REPO_ROOT", os.getcwd())
-    logdir = os.path.join(root, "gpurun_out")
+    progress, and also a file fullsize_progress.log in the folder named by
+    MALA_PROGRESS_DIR when that variable is set."""
+    logdir = os.environ.get("MALA_PROGRESS_DIR", "")
     t0 = time.time()
 
     def _say(msg):
         line = f"[{time.time() - t0:7.1f}s] {msg}"
         with capsys.disabled():
             print(line, flush=True)
-        if os.path.isdir(logdir):
+        if logdir and os.path.isdir(logdir):
             with open(os.path.join(logdir, "fullsize_progress.log"), "a") as f:
                 f.write(line + "\n")
     return _say
