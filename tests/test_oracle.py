@@ -496,6 +496,56 @@ def test_lazy_reference_changes_where_p_is_rounded_not_the_result():
     assert np.abs(b["lse"] - e["lse"]).max() < 1e-5
 
 
+def _np_bf16_forward(q, k, v, bk, lazy):
+    """Restatement in NumPy, row by row, of the forward with every legal tile
+    retained (tau = 0) and P~ rounded to bf16 (torch's cast, through fp32)
+    before the P V product: tiles from the diagonal down, the exponentials
+    against the running maximum, or with `lazy` against a reference that
+    moves only when a tile's row maximum exceeds it by more than 8 ln 2."""
+    def bf(x):
+        return torch.tensor(x, dtype=torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    B, Hq, N, d = q.shape
+    G = Hq // k.shape[1]
+    scale = 1.0 / np.sqrt(d)
+    o = np.zeros_like(q)
+    for b in range(B):
+        for h in range(Hq):
+            s = scale * q[b, h] @ k[b, h // G].T
+            for r in range(N):
+                m, l, acc = -np.inf, 0.0, np.zeros(d)
+                for j in range(r // bk, -1, -1):
+                    st = s[r, j * bk:min(N, j * bk + bk)].copy()
+                    st[np.arange(j * bk, j * bk + st.size) > r] = -np.inf
+                    mt = st.max()
+                    if mt == -np.inf:
+                        continue
+                    m_new = (mt if mt > m + 8.0 * np.log(2.0) else m) if lazy else max(m, mt)
+                    alpha = np.exp(m - m_new) if m > -np.inf else 0.0
+                    pt = np.exp(st - m_new)
+                    acc = alpha * acc + bf(pt) @ v[b, h // G, j * bk:j * bk + st.size]
+                    l = alpha * l + pt.sum()
+                    m = m_new
+                o[b, h, r] = acc / l
+    return bf(o)
+
+
+def test_lazy_reference_model_matches_a_numpy_restatement():
+    """The LAZY_REF model rounds P~ as a plain restatement of the lazy rule
+    does, and the plain model as one with the running maximum: the two
+    models differ only in the reference rule."""
+    q, k, v, do = _gen_small(N=160, Hq=2, Hkv=1, d=16, planted=4, seed=23)
+    for lazy, flags in ((True, O.BF16_FWD | O.LAZY_REF), (False, O.BF16_FWD)):
+        r = O.mala_fwd(q, k, v, 0.0, True, 16, 16, round_flags=flags)
+        e = _np_bf16_forward(q, k, v, 16, lazy)
+        diff = np.abs(r["o"] - e)
+        # identical up to a rare bf16 flip at a rounding boundary
+        assert (diff == 0).mean() > 0.999
+        assert diff.max() <= 2.0 ** -7 * np.abs(e).max()
+    a = O.mala_fwd(q, k, v, 0.0, True, 16, 16, round_flags=O.BF16_FWD | O.LAZY_REF)
+    b = O.mala_fwd(q, k, v, 0.0, True, 16, 16, round_flags=O.BF16_FWD)
+    assert not np.array_equal(a["o"], b["o"])  # the rule is exercised
+
+
 # ------------------------------------------------------- magnitude mode ----
 
 def test_magnitude_mode_bounds_and_matches_twin():

@@ -18,6 +18,9 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "mala_oracle.c")
 
 MUTANTS = {
+    # the kernel's rounding model: the reference moves on jumps of more than 8 log2 units
+    "lazy reference at 4 log2 units": ("m_new = mt[r] > m[r] + 8.0 * 0.69314718055994530942 ? mt[r] : m[r];",
+                                       "m_new = mt[r] > m[r] + 4.0 * 0.69314718055994530942 ? mt[r] : m[r];"),
     # Sec. 2.1: L_q counts the query's own key
     "L_q one short": ("return p->causal ? (double)(q + causal_offset(p) + 1) : (double)p->seqlen_k;",
                       "return p->causal ? (double)(q + causal_offset(p)) + 1e-9 : (double)p->seqlen_k;"),
