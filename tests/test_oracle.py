@@ -546,6 +546,48 @@ def test_lazy_reference_model_matches_a_numpy_restatement():
     assert not np.array_equal(a["o"], b["o"])  # the rule is exercised
 
 
+def test_bf16_backward_model_matches_a_numpy_restatement():
+    """The backward's bf16-operand model (Algorithm 2 with every legal tile
+    kept): P from the saved LSE and dS = P (dP - D) with D = rowsum(O dO),
+    P rounded to bf16 before the dV product and dS before the dK and dQ
+    products, the softmax scale applied to the sums, outputs rounded. A plain
+    NumPy restatement with torch's bf16 cast gives the same gradients."""
+    q, k, v, do = _gen_small(N=150, Hq=4, Hkv=2, d=16, planted=4, seed=29)
+    f = O.mala_fwd(q, k, v, 0.0, True, 16, 16)
+    r = O.mala_bwd(q, k, v, f["o"], f["lse"], do, 0.0, True, 16, 16, round_flags=O.BF16_BWD)
+
+    def bf(x):
+        return torch.tensor(x, dtype=torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    B, Hq, N, d = q.shape
+    G = Hq // k.shape[1]
+    scale = 1.0 / np.sqrt(d)
+    legal = np.tril(np.ones((N, N), dtype=bool))
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            s = scale * q[b, h] @ k[b, g].T
+            p = np.where(legal, np.exp(s - f["lse"][b, h][:, None]), 0.0)
+            dp = do[b, h] @ v[b, g].T
+            D = (f["o"][b, h] * do[b, h]).sum(-1)
+            ds = np.where(legal, p * (dp - D[:, None]), 0.0)
+            dq[b, h] = scale * (bf(ds) @ k[b, g])
+            dk[b, g] += bf(ds).T @ q[b, h]
+            dv[b, g] += bf(p).T @ do[b, h]
+    dk *= scale
+    for name, e in (("dq", dq), ("dk", dk), ("dv", dv)):
+        e = bf(e)
+        diff = np.abs(r[name] - e)
+        # one bf16 step where the two summation orders round apart, and an
+        # fp64-noise floor for elements that cancel to almost nothing (where
+        # dP - D itself is rounding noise of order 1e-16)
+        assert (diff <= 2.0 ** -8 * np.abs(e) + 1e-9 * np.abs(e).max()).all(), name
+        assert (diff == 0).mean() > 0.98, name
+    # and the rounding is exercised: the exact gradients differ
+    x = O.mala_bwd(q, k, v, f["o"], f["lse"], do, 0.0, True, 16, 16)
+    assert not np.array_equal(x["dq"], r["dq"])
+
+
 # ------------------------------------------------------- magnitude mode ----
 
 def test_magnitude_mode_bounds_and_matches_twin():

@@ -18,6 +18,9 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "mala_oracle.c")
 
 MUTANTS = {
+    # the backward's bf16-operand model rounds dS before the dK / dQ products
+    "bf16 model without dS rounding": ("double du = (p->round_flags & ORC_ROUND_DS) ? round_bf16(ds) : ds;",
+                                       "double du = ds;"),
     # the kernel's rounding model: the reference moves on jumps of more than 8 log2 units
     "lazy reference at 4 log2 units": ("m_new = mt[r] > m[r] + 8.0 * 0.69314718055994530942 ? mt[r] : m[r];",
                                        "m_new = mt[r] > m[r] + 4.0 * 0.69314718055994530942 ? mt[r] : m[r];"),
