@@ -1,6 +1,7 @@
-"""Host logic of bench.py that runs without a GPU (test code): the one-GPU
-guard, and the rule that a committed HBM-traffic summary is reported only
-while the kernel sources match the ones its counters were taken with."""
+"""Host logic that runs without a GPU (test code): the one-GPU guard of
+bench.py, the rule that a committed HBM-traffic summary is reported only
+while the kernel sources match the ones its counters were taken with, and
+the host model of the backward's schedule against the kernels' constants."""
 import os
 import subprocess
 import sys
@@ -54,3 +55,23 @@ def test_committed_profiles_name_their_commands():
                  "mala_decode_traffic_128k.txt", "sq_counters_128k.txt", "sq_activity_128k.txt"):
         text = open(os.path.join(ROOT, "profiles", name)).read()
         assert "rocprofv3" in text and "bench.py" in text, name
+
+
+def test_host_schedule_model_uses_the_kernels_constants():
+    """tests/bwd_schedule.py restates the dK/dV pass's pairing and
+    segmentation rule to choose the key blocks the full-size tests compare;
+    its constants must be the kernels' (items per segment, segments per
+    pair, partial-sum slots per pair)."""
+    import re
+
+    import bwd_schedule as S
+    csrc = os.path.join(ROOT, "adaptive_softmax_attention_amd", "csrc")
+    text = open(os.path.join(csrc, "mala_internal.h")).read() + open(os.path.join(csrc, "mala_bwd.hip")).read()
+
+    def const(name):
+        m = re.search(r"constexpr int " + name + r"\s*=\s*(\d+)\s*;", text)
+        assert m, name
+        return int(m.group(1))
+    assert S.SEG_KEPT == const("kSegKept")
+    assert S.SEG_MAX == const("kSegMax")
+    assert S.SLOTS_PER_PAIR == const("kSlotsPerPair")
