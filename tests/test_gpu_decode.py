@@ -200,13 +200,12 @@ def run_decode_paged(pin, tau, S, dense=False, lens=None, bk=64):
     return o, lse, st.decisions.cpu().numpy().astype(np.int8), st.counters.cpu().numpy()
 
 
-@pytest.mark.parametrize("tau,S", [(1.0, 3), (0.0, 2), (4.0, 1)])
-def test_decode_paged_varlen(tau, S):
-    """Each sequence against the oracle's decode of its own cache (its own
-    L = cache length), with the same decision, V1/V2 and LSE checks."""
-    lens = [1, 63, 64, 700, 1000]
-    pin = paged_inputs(41, lens, 8, 2, 128)
-    o, lse, dec, cnt = run_decode_paged(pin, tau, S)
+def compare_decode_paged(pin, lens, tau, S, bk=64):
+    """Paged decode of the sequences `lens` against the oracle's decode of
+    each sequence's own cache (its own L = cache length), with the decision,
+    V1/V2 and LSE checks of compare_decode; tiles past a sequence are never
+    tested, and the counters match the bitmaps."""
+    o, lse, dec, cnt = run_decode_paged(pin, tau, S, bk=bk)
     go, gl = gpu_to_f64(o), lse.cpu().numpy().astype(np.float64)
     assert np.isfinite(go).all() and np.isfinite(gl).all()
     legal_total = kept_total = 0
@@ -214,12 +213,12 @@ def test_decode_paged_varlen(tau, S):
         q = bits_to_f64(pin["q"][b:b + 1])
         k = bits_to_f64(pin["k"][b:b + 1, :, :n])
         v = bits_to_f64(pin["v"][b:b + 1, :, :n])
-        nt = -(-n // 64)
+        nt = -(-n // bk)
         gd = dec[b:b + 1, :, :nt]
         assert (dec[b, :, nt:] == -1).all()  # tiles past the sequence are never tested
 
         def run(force, flags=O.EXACT):
-            return O.mala_decode(q, k, v, S, tau, 64, round_flags=flags, force=force)
+            return O.mala_decode(q, k, v, S, tau, bk, round_flags=flags, force=force)
 
         free = run(None)
         legal = free["dec"] >= 0
@@ -234,6 +233,14 @@ def test_decode_paged_varlen(tau, S):
         legal_total += int(legal.sum())
         kept_total += int((gd == 1).sum())
     assert cnt[0] == legal_total and cnt[1] == kept_total
+
+
+@pytest.mark.parametrize("tau,S", [(1.0, 3), (0.0, 2), (4.0, 1)])
+def test_decode_paged_varlen(tau, S):
+    """Each sequence against the oracle's decode of its own cache (its own
+    L = cache length), with the same decision, V1/V2 and LSE checks."""
+    lens = [1, 63, 64, 700, 1000]
+    compare_decode_paged(paged_inputs(41, lens, 8, 2, 128), lens, tau, S)
 
 
 @pytest.mark.parametrize("bk", [64, 128])

@@ -17,12 +17,9 @@ import math
 import numpy as np
 import pytest
 
-import oracle as O
 import workloads as W
-from parity import (LSE_TOL, V2_TOL, bits_to_f64, check_decisions, gpu_to_f64, settle_fwd_branch,
-                    v1_ok, v2)
 from test_gpu_bwd import compare_bwd
-from test_gpu_decode import compare_decode, decode_inputs, paged_inputs, run_decode_paged
+from test_gpu_decode import compare_decode, compare_decode_paged, decode_inputs, paged_inputs
 from test_gpu_fwd import compare_fwd
 
 pytestmark = pytest.mark.gpu
@@ -115,35 +112,7 @@ def test_random_decode_paged(case):
     S = min(c["S"], -(-max(lens) // bk))
     print(f"[random paged] seed {seed} lens {lens} Hq {c['Hq']} Hkv {c['Hkv']} d {c['d']} "
           f"tau {tau} S {S} bk {bk}", flush=True)
-    pin = paged_inputs(seed, lens, c["Hq"], c["Hkv"], c["d"])
-    o, lse, dec, cnt = run_decode_paged(pin, tau, S, bk=bk)
-    go, gl = gpu_to_f64(o), lse.cpu().numpy().astype(np.float64)
-    assert np.isfinite(go).all() and np.isfinite(gl).all()
-    legal_total = kept_total = 0
-    for b, n in enumerate(lens):
-        q = bits_to_f64(pin["q"][b:b + 1])
-        k = bits_to_f64(pin["k"][b:b + 1, :, :n])
-        v = bits_to_f64(pin["v"][b:b + 1, :, :n])
-        nt = -(-n // bk)
-        gd = dec[b:b + 1, :, :nt]
-        assert (dec[b, :, nt:] == -1).all()
-
-        def run(force, flags=O.EXACT):
-            return O.mala_decode(q, k, v, S, tau, bk, round_flags=flags, force=force)
-
-        free = run(None)
-        legal = free["dec"] >= 0
-        check_decisions(gd, free, legal)
-        ex, _ = settle_fwd_branch(run, gd, legal, free=free)
-        bf = run(ex["dec"].copy(), O.BF16_DECODE)
-        mag = run(ex["dec"].copy(), O.BF16_DECODE | O.ABS)
-        ok, worst = v1_ok(go[b:b + 1], bf["o"], mag["o"])
-        assert ok, f"sequence {b}: V1 worst ratio {worst}"
-        assert v2(go[b:b + 1], bf["o"]) <= V2_TOL
-        assert np.abs(gl[b:b + 1] - ex["lse"]).max() <= LSE_TOL
-        legal_total += int(legal.sum())
-        kept_total += int((gd == 1).sum())
-    assert cnt[0] == legal_total and cnt[1] == kept_total
+    compare_decode_paged(paged_inputs(seed, lens, c["Hq"], c["Hkv"], c["d"]), lens, tau, S, bk=bk)
 
 
 def _draw_medium(seed):
