@@ -15,9 +15,10 @@
  *
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller. The library
- *     keeps no state between calls, allocates no memory, never synchronises
- *     the device, and enqueues all work on `stream` (a hipStream_t; NULL is
- *     the default stream).
+ *     allocates no memory, never synchronises the device, and enqueues all
+ *     work on `stream` (a hipStream_t; NULL is the default stream). Between
+ *     calls it keeps only a per-device record of the architecture check and,
+ *     for mala_decode_noalloc, of its device array's address.
  *   - Layouts are contiguous row-major:
  *       Q, O, dO, dQ   [batch][heads_q ][seqlen_q][head_dim]  bf16
  *       K, V, dK, dV   [batch][heads_kv][seqlen_k][head_dim]  bf16
