@@ -44,8 +44,9 @@ ROUND_OUT = 8
 ABS = 16  # magnitude mode: sums of |a|*|b| instead of a*b (error-bound scale)
 ABS_D = 32  # backward: dS -> P * sum_d |O||dO| in dQ / dK (sensitivity to D)
 # forward model: exponentials against a reference maximum that moves only on
-# jumps of more than 8 log2 units (where the kernel rounds P); exact results
-# are the same for either reference
+# jumps of more than 8 log2 units (where the kernel rounds P), a 128-key tile
+# whose upper 64 keys pass alone taken as those 64 keys and then the lower 64;
+# exact results are the same for either reference
 LAZY_REF = 64
 EXACT = 0
 BF16_FWD = ROUND_P_FWD | ROUND_OUT

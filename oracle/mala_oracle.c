@@ -67,9 +67,12 @@
                               tile are taken against a reference maximum that
                               moves only when a tile's row maximum exceeds it by
                               more than 8 log2 units (P <= 2^8), as the kernel
-                              forms them. In exact arithmetic m + log l, and so
-                              the test and the result, are the same for either
-                              reference; what changes is where P~ is rounded */
+                              forms them; a 128-key tile whose upper 64 keys
+                              pass the test alone updates as those 64 keys and
+                              then the lower 64, each moving the reference. In
+                              exact arithmetic m + log l, and so the test and
+                              the result, are the same for either reference;
+                              what changes is where P~ is rounded */
 
 typedef struct {
   int32_t batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim;
@@ -255,6 +258,42 @@ int orc_dense_bwd(const orc_problem* p, const double* q, const double* k,
 /* ------------------------------------------------------------------------ */
 /* MALA forward (Algorithm 1; Eqs. 1-3)                                       */
 
+/* Online-softmax update (Sec. 2.2; Algorithm 1) of every valid row by the
+ * columns [c0, c1) of a retained tile whose scores are s (bk per row, -inf
+ * where not legal): m_new from the row maximum over those columns, the
+ * rescale of l and acc, and the exponentials added to l and, times V, to acc. */
+static void online_update(const orc_problem* p, const double* s, int bk, const double* vbase,
+                          int64_t k0, int64_t nrows, int c0, int c1, double* m, double* l,
+                          double* acc) {
+  const int d = p->head_dim;
+  for (int64_t r = 0; r < nrows; ++r) {
+    double mx = -INFINITY;
+    for (int c = c0; c < c1; ++c)
+      if (s[r * bk + c] > mx) mx = s[r * bk + c];
+    double m_new = mx > m[r] ? mx : m[r];
+    if (p->round_flags & ORC_LAZY_REF) /* 8 log2 units = 8 ln 2 nats */
+      m_new = mx > m[r] + 8.0 * 0.69314718055994530942 ? mx : m[r];
+    if (m_new == -INFINITY) continue;
+    const double alpha = (m[r] == -INFINITY) ? 0.0 : exp(m[r] - m_new);
+    double rowsum = 0.0;
+    for (int c = 0; c < d; ++c) acc[r * d + c] *= alpha;
+    for (int c = c0; c < c1; ++c) {
+      const double sv = s[r * bk + c];
+      if (sv == -INFINITY) continue;
+      const double pt = exp(sv - m_new);
+      rowsum += pt;
+      const double pu = (p->round_flags & ORC_ROUND_P_FWD) ? round_bf16(pt) : pt;
+      const double* vv = vbase + (k0 + c) * d;
+      if (p->round_flags & ORC_ABS)
+        for (int e = 0; e < d; ++e) acc[r * d + e] += pu * fabs(vv[e]);
+      else
+        for (int e = 0; e < d; ++e) acc[r * d + e] += pu * vv[e];
+    }
+    l[r] = alpha * l[r] + rowsum;
+    m[r] = m_new;
+  }
+}
+
 /* Runs the online rule for one query-row block over key blocks
  * [j_lo, j_hi] visited in descending order and returns the unnormalised
  * running state (m, l, acc) per row, which the forward finalises and the
@@ -312,30 +351,33 @@ static void online_block(const orc_problem* p, const double* q, int64_t q_stride
     if (dec) dec[j] = retain ? ORC_RETAIN : ORC_SKIP;
     if (mrg) mrg[j] = tile_margin;
     if (!retain) continue; /* m, l, O unchanged */
-    /* retained tile: online-softmax update of every valid row */
-    for (int64_t r = 0; r < nrows; ++r) {
-      double m_new = mt[r] > m[r] ? mt[r] : m[r];
-      if (p->round_flags & ORC_LAZY_REF) /* 8 log2 units = 8 ln 2 nats */
-        m_new = mt[r] > m[r] + 8.0 * 0.69314718055994530942 ? mt[r] : m[r];
-      if (m_new == -INFINITY) continue;
-      const double alpha = (m[r] == -INFINITY) ? 0.0 : exp(m[r] - m_new);
-      double rowsum = 0.0;
-      for (int c = 0; c < d; ++c) acc[r * d + c] *= alpha;
-      for (int c = 0; c < bk; ++c) {
-        const double sv = s[r * bk + c];
-        if (sv == -INFINITY) continue;
-        const double pt = exp(sv - m_new);
-        rowsum += pt;
-        const double pu = (p->round_flags & ORC_ROUND_P_FWD) ? round_bf16(pt) : pt;
-        const double* vv = vbase + (k0 + c) * d;
-        if (p->round_flags & ORC_ABS)
-          for (int e = 0; e < d; ++e) acc[r * d + e] += pu * fabs(vv[e]);
-        else
-          for (int e = 0; e < d; ++e) acc[r * d + e] += pu * vv[e];
+    /* retained tile: online-softmax update of every valid row. In the
+     * lazy-reference model a 128-key tile is formed as the kernel forms it,
+     * as two 64-key halves: when the upper half passes the test on its own
+     * (against the state before the tile), the halves update in turn, upper
+     * first, each moving the reference by its own row maxima; otherwise both
+     * are exponentiated against one reference. In exact arithmetic the two
+     * orders give the same result (Sec. 2.2); they differ only in where P~
+     * is rounded. */
+    if ((p->round_flags & ORC_LAZY_REF) && bk == 128) {
+      double hi_margin = -INFINITY;
+      for (int64_t r = 0; r < nrows; ++r) {
+        double mh = -INFINITY;
+        for (int c = 64; c < 128; ++c)
+          if (s[r * bk + c] > mh) mh = s[r * bk + c];
+        if (mh == -INFINITY) continue;
+        const double mg = (l[r] == 0.0)
+                              ? INFINITY
+                              : mh - (m[r] + log(l[r])) - log_threshold(p, q0 + r);
+        if (mg > hi_margin) hi_margin = mg;
       }
-      l[r] = alpha * l[r] + rowsum;
-      m[r] = m_new;
+      if (!(hi_margin < 0.0)) {
+        online_update(p, s, bk, vbase, k0, nrows, 64, 128, m, l, acc);
+        online_update(p, s, bk, vbase, k0, nrows, 0, 64, m, l, acc);
+        continue;
+      }
     }
+    online_update(p, s, bk, vbase, k0, nrows, 0, bk, m, l, acc);
   }
   free(s);
   free(mt);

@@ -145,3 +145,15 @@ def test_random_medium_backward(case):
     print(f"[random medium bwd] seed {seed} {c}", flush=True)
     compare_bwd(_prefill(seed, c, True), c["tau"], causal=c["causal"], label=f"rmed{case}",
                 bq=c["bq"], bk=c["bk"])
+
+
+@pytest.mark.parametrize("seed", [80092])
+def test_random_forward_found_by_a_wider_sweep(seed):
+    """A case a wider run of this sweep found: 70 keys in one 128-key
+    decision tile, diffuse non-causal rows. The kernel forms the tile's upper
+    64 keys, which pass on their own, before the lower 64, each with its own
+    lazy reference step; the bf16 model must round P~ the same way."""
+    c = _draw(seed)
+    print(f"[random fwd] seed {seed} {c}", flush=True)
+    compare_fwd(_prefill(seed, c, False), c["tau"], causal=c["causal"], label=f"seed{seed}",
+                bq=c["bq"], bk=c["bk"])

@@ -496,12 +496,16 @@ def test_lazy_reference_changes_where_p_is_rounded_not_the_result():
     assert np.abs(b["lse"] - e["lse"]).max() < 1e-5
 
 
-def _np_bf16_forward(q, k, v, bk, lazy):
-    """Restatement in NumPy, row by row, of the forward with every legal tile
-    retained (tau = 0) and P~ rounded to bf16 (torch's cast, through fp32)
-    before the P V product: tiles from the diagonal down, the exponentials
-    against the running maximum, or with `lazy` against a reference that
-    moves only when a tile's row maximum exceeds it by more than 8 ln 2."""
+def _np_bf16_forward(q, k, v, bq, bk, lazy):
+    """Restatement in NumPy, row by row, of the causal forward with every
+    legal tile retained (tau = 0) and P~ rounded to bf16 (torch's cast,
+    through fp32) before the P V product: tiles from the diagonal down, the
+    exponentials against the running maximum, or with `lazy` against a
+    reference that moves only when a tile's row maximum exceeds it by more
+    than 8 ln 2. With `lazy`, a 128-key tile whose upper 64 keys hold a legal
+    key for some row of the query block (so that they pass at tau = 0 on
+    their own) is taken as those 64 keys and then the lower 64, each with its
+    own reference step; otherwise as one."""
     def bf(x):
         return torch.tensor(x, dtype=torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
     B, Hq, N, d = q.shape
@@ -511,20 +515,28 @@ def _np_bf16_forward(q, k, v, bk, lazy):
     for b in range(B):
         for h in range(Hq):
             s = scale * q[b, h] @ k[b, h // G].T
+            vv = v[b, h // G]
             for r in range(N):
                 m, l, acc = -np.inf, 0.0, np.zeros(d)
-                for j in range(r // bk, -1, -1):
-                    st = s[r, j * bk:min(N, j * bk + bk)].copy()
-                    st[np.arange(j * bk, j * bk + st.size) > r] = -np.inf
-                    mt = st.max()
-                    if mt == -np.inf:
-                        continue
-                    m_new = (mt if mt > m + 8.0 * np.log(2.0) else m) if lazy else max(m, mt)
-                    alpha = np.exp(m - m_new) if m > -np.inf else 0.0
-                    pt = np.exp(st - m_new)
-                    acc = alpha * acc + bf(pt) @ v[b, h // G, j * bk:j * bk + st.size]
-                    l = alpha * l + pt.sum()
-                    m = m_new
+                r_last = min(N - 1, (r // bq) * bq + bq - 1)  # the block's last row
+                for j in range(r_last // bk, -1, -1):
+                    k0 = j * bk
+                    st = s[r, k0:min(N, k0 + bk)].copy()
+                    st[np.arange(k0, k0 + st.size) > r] = -np.inf
+                    parts = [(0, st.size)]
+                    if lazy and bk == 128 and k0 + 64 <= r_last:
+                        parts = [(64, st.size), (0, 64)]  # upper half first
+                    for c0, c1 in parts:
+                        sp = st[c0:c1]
+                        mt = sp.max() if sp.size else -np.inf
+                        m_new = (mt if mt > m + 8.0 * np.log(2.0) else m) if lazy else max(m, mt)
+                        if m_new == -np.inf:
+                            continue
+                        alpha = np.exp(m - m_new) if m > -np.inf else 0.0
+                        pt = np.exp(sp - m_new)
+                        acc = alpha * acc + bf(pt) @ vv[k0 + c0:k0 + c0 + sp.size]
+                        l = alpha * l + pt.sum()
+                        m = m_new
                 o[b, h, r] = acc / l
     return bf(o)
 
@@ -536,7 +548,7 @@ def test_lazy_reference_model_matches_a_numpy_restatement():
     q, k, v, do = _gen_small(N=160, Hq=2, Hkv=1, d=16, planted=4, seed=23)
     for lazy, flags in ((True, O.BF16_FWD | O.LAZY_REF), (False, O.BF16_FWD)):
         r = O.mala_fwd(q, k, v, 0.0, True, 16, 16, round_flags=flags)
-        e = _np_bf16_forward(q, k, v, 16, lazy)
+        e = _np_bf16_forward(q, k, v, 16, 16, lazy)
         diff = np.abs(r["o"] - e)
         # identical up to a rare bf16 flip at a rounding boundary
         assert (diff == 0).mean() > 0.999
@@ -544,6 +556,23 @@ def test_lazy_reference_model_matches_a_numpy_restatement():
     a = O.mala_fwd(q, k, v, 0.0, True, 16, 16, round_flags=O.BF16_FWD | O.LAZY_REF)
     b = O.mala_fwd(q, k, v, 0.0, True, 16, 16, round_flags=O.BF16_FWD)
     assert not np.array_equal(a["o"], b["o"])  # the rule is exercised
+
+
+def test_lazy_reference_model_128_key_tiles_in_halves():
+    """With 128-key tiles the LAZY_REF model takes a tile whose upper 64 keys
+    pass on their own as those keys and then the lower 64 (the NumPy
+    restatement above); a model that takes every tile as one differs."""
+    q, k, v, do = _gen_small(N=400, Hq=2, Hkv=1, d=16, planted=6, seed=31, sigma=0.5)
+    r = O.mala_fwd(q, k, v, 0.0, True, 64, 128, round_flags=O.BF16_FWD | O.LAZY_REF)
+    e = _np_bf16_forward(q, k, v, 64, 128, True)
+    diff = np.abs(r["o"] - e)
+    assert (diff == 0).mean() > 0.999
+    assert diff.max() <= 2.0 ** -7 * np.abs(e).max()
+    # the exact result does not depend on how the tile is split
+    x = O.mala_fwd(q, k, v, 0.0, True, 64, 128)
+    y = O.mala_fwd(q, k, v, 0.0, True, 64, 64)
+    assert np.allclose(x["o"], y["o"], rtol=1e-12, atol=1e-12)
+    assert np.allclose(x["lse"], y["lse"], rtol=1e-12, atol=1e-12)
 
 
 def test_bf16_backward_model_matches_a_numpy_restatement():

@@ -22,8 +22,11 @@ MUTANTS = {
     "bf16 model without dS rounding": ("double du = (p->round_flags & ORC_ROUND_DS) ? round_bf16(ds) : ds;",
                                        "double du = ds;"),
     # the kernel's rounding model: the reference moves on jumps of more than 8 log2 units
-    "lazy reference at 4 log2 units": ("m_new = mt[r] > m[r] + 8.0 * 0.69314718055994530942 ? mt[r] : m[r];",
-                                       "m_new = mt[r] > m[r] + 4.0 * 0.69314718055994530942 ? mt[r] : m[r];"),
+    "lazy reference at 4 log2 units": ("m_new = mx > m[r] + 8.0 * 0.69314718055994530942 ? mx : m[r];",
+                                       "m_new = mx > m[r] + 4.0 * 0.69314718055994530942 ? mx : m[r];"),
+    # the same model forms a 128-key tile whose upper 64 keys pass alone as two halves
+    "lazy reference over whole 128-key tiles": ("if ((p->round_flags & ORC_LAZY_REF) && bk == 128) {",
+                                                "if (0) {"),
     # Sec. 2.1: L_q counts the query's own key
     "L_q one short": ("return p->causal ? (double)(q + causal_offset(p) + 1) : (double)p->seqlen_k;",
                       "return p->causal ? (double)(q + causal_offset(p)) + 1e-9 : (double)p->seqlen_k;"),
@@ -48,9 +51,11 @@ MUTANTS = {
     "no rescale of l": ("l[r] = alpha * l[r] + rowsum;", "l[r] = l[r] + rowsum;"),
     # Sec. 2.2: every valid row of a retained tile is updated
     "update only passing rows": (
-        "      if (m_new == -INFINITY) continue;\n      const double alpha",
-        "      if (m_new == -INFINITY) continue;\n      if (l[r] != 0.0 && mt[r] - (m[r] + log(l[r])) - "
-        "log_threshold(p, q0 + r) < 0) continue;\n      const double alpha"),
+        "    online_update(p, s, bk, vbase, k0, nrows, 0, bk, m, l, acc);\n  }\n  free(s);",
+        "    for (int64_t r = 0; r < nrows; ++r)\n"
+        "      if (l[r] != 0.0 && mt[r] - (m[r] + log(l[r])) - log_threshold(p, q0 + r) < 0)\n"
+        "        for (int c = 0; c < bk; ++c) s[r * bk + c] = -INFINITY;\n"
+        "    online_update(p, s, bk, vbase, k0, nrows, 0, bk, m, l, acc);\n  }\n  free(s);"),
     # GQA: consecutive query heads share a KV head
     "GQA head map": ("    const int64_t g = h / G;\n    const int64_t q0",
                      "    const int64_t g = h % p->heads_kv;\n    const int64_t q0"),
