@@ -334,9 +334,11 @@ __global__ __launch_bounds__(576, 1) void bwd_score_kernel(BwdParams p) {
         const char* qt = ring + slot * SQ;
         const float* wr = (const float*)(qt + TB);
         const bool need_mask = diag_tile(p, i, jw) || (64 * jw + 64 > p.nk);
-        bool hit = false;
-#pragma unroll
-        for (int qs = 0; qs < 2; ++qs) {
+        // the tile is kept as soon as one legal entry passes: the second
+        // 32-column half is scored only if the first has no passing entry
+        // (the dense path keeps every legal tile and scores nothing)
+        bool want = !kTest;
+        for (int qs = 0; qs < 2 && !want; ++qs) {
           // B operands (Q^T: column 32 qs + l32) up front, then the products
           bf16x8 bq[NDC];
 #pragma unroll
@@ -354,6 +356,11 @@ __global__ __launch_bounds__(576, 1) void bwd_score_kernel(BwdParams p) {
           for (int dc = 0; dc < NDC; ++dc)
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) s[kt] = mfma32x32x16(kreg[kt][dc], bq[dc], s[kt]);
+          // every operand read is issued before the first product, so that
+          // later reads land while earlier products run (left to itself the
+          // scheduler alternates one read, a full wait and two products)
+          __builtin_amdgcn_sched_group_barrier(0x100, NDC, 0);    // LDS reads
+          __builtin_amdgcn_sched_group_barrier(0x008, 2 * NDC, 0);  // products
           // register 4e' + r of subtile kt holds key 32 kt + 8e' + 4hh + r
           // of query column 32 qs + l32
           if (need_mask) {
@@ -375,9 +382,8 @@ __global__ __launch_bounds__(576, 1) void bwd_score_kernel(BwdParams p) {
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kt][e]);
-          hit = hit || mx >= wr[32 * qs + l32];
+          want = wave_any(mx >= wr[32 * qs + l32]);
         }
-        const bool want = kTest ? wave_any(hit) : true;
         kept += want ? 1 : 0;
         if (lane == 0) {
           const int bh = b * p.heads_q + kvh * p.group + ch;
@@ -624,6 +630,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
   constexpr int RB = 2 * 64 * 4;         // z2 and D of the 64 rows
   constexpr int CPW = TB / 16 / NT;      // 16-byte copies per lane per tile
   constexpr int OPS = 2 * CPW + 1;       // copies per wave per list entry
+  static_assert(2 * OPS < 64, "vmcnt range");
   constexpr int RP = 4;                  // ring: the entry in use + 3 ahead
   constexpr int SP = 2 * TB + RB;        // ring slot: Q, dO, row terms
   constexpr int CH = 2048;               // items per chunk
@@ -798,7 +805,11 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     int issued = 0;
     for (; issued < RP - 1 && issued < n_list; ++issued) issue_post(issued);
     for (int t = 0; t < n_list; ++t) {
-      vmcnt_wait_le((issued - (t + 1)) * OPS);  // entry t landed
+      // entry t landed: at most two later entries in flight (a fixed count
+      // per case, no run-time selection among all possible counts)
+      if (issued - (t + 1) >= 2) vmcnt_wait<2 * OPS>();
+      else if (issued - (t + 1) == 1) vmcnt_wait<OPS>();
+      else vmcnt_wait<0>();
       lds_barrier();  // entry t visible; every wave is done with entry t - 1
       if (issued < n_list) {  // into the slot of entry t - 1
         issue_post(issued);
