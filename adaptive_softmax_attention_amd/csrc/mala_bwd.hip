@@ -257,7 +257,7 @@ __global__ __launch_bounds__(576, 1) void bwd_score_kernel(BwdParams p) {
     // the 32-row operand reads expect (rows past the end re-read the last
     // row), then the 64 thresholds
     int fi = p.tr - 1, fh = 0;  // query block and group head of the next item fetched
-    auto fetch = [&](char* slot) {
+    auto fetch = [&](uint32_t slot) {
       const int h = kvh * p.group + fh, i = fi;
       const __bf16* rows0 = p.q + ((size_t)(b * p.heads_q + h) * p.nq + (size_t)64 * i) * D;
       const int last = p.nq - 1 - 64 * i;  // last row inside the queries
@@ -267,10 +267,10 @@ __global__ __launch_bounds__(576, 1) void bwd_score_kernel(BwdParams p) {
         const int row = s / KCH, pc = s % KCH;
         const uint32_t voff =
             (uint32_t)((min(row, last) * D + ((pc ^ kswz32<D>(row)) & (KCH - 1)) * 8) * 2);
-        async_copy16_so(rows0, voff, slot + x * 1024);
+        async_copy16_sa(rows0, voff, slot + x * 1024);
       }
       const float* ri = p.rowinfo + ((size_t)(b * p.heads_q + h) * p.tr + i) * kRowInfo + 64;
-      if (lane < 16) async_copy16_so(ri, (uint32_t)(16 * lane), slot + TB);
+      if (lane < 16) async_copy16_sa(ri, (uint32_t)(16 * lane), slot + TB);
     };
     auto publish = [&](int it) {
       if (lane == 0)
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(576, 1) void bwd_score_kernel(BwdParams p) {
           });
         }
       }
-      fetch(ring + (nf % RQ) * SQ);
+      fetch(lds_addr(ring) + (uint32_t)((nf % RQ) * SQ));
       if (++fh == p.group) {
         fh = 0;
         --fi;
@@ -712,6 +712,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
 
   // ---- asynchronous tile copies: each wave moves a quarter of a tile and
   //      eight of the 32 row-term chunks ----
+  const uint32_t ring_lds = lds_addr(ring);
   uint32_t toff[CPW];  // byte offset within a full tile, per copy
 #pragma unroll
   for (int x = 0; x < CPW; ++x) {
@@ -719,28 +720,28 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     const int row = s / KCH, pc = s % KCH;
     toff[x] = (uint32_t)(row * D * 2 + ((pc ^ qswz32<D>(row)) & (KCH - 1)) * 16);
   }
-  auto copy_tile = [&](const __bf16* rows0, int i, char* slot) {
+  auto copy_tile = [&](const __bf16* rows0, int i, uint32_t slot) {
     // rows0: row 0 of (b, h); block i lands swizzled in slot
     if (64 * i + 64 <= p.nq) {
       const char* src = (const char*)(rows0 + (size_t)64 * i * D);
 #pragma unroll
-      for (int x = 0; x < CPW; ++x) async_copy16_so(src, toff[x], slot + (4 * x + w) * 1024);
+      for (int x = 0; x < CPW; ++x) async_copy16_sa(src, toff[x], slot + (4 * x + w) * 1024);
     } else {  // ragged last block: rows past the end re-read the last row
 #pragma unroll
       for (int x = 0; x < CPW; ++x) {
         const int s = (4 * x + w) * 64 + lane;
         const int row = s / KCH, pc = s % KCH;
         const int qq = min(64 * i + row, p.nq - 1);
-        async_copy16(rows0 + (size_t)qq * D + ((pc ^ qswz32<D>(row)) & (KCH - 1)) * 8,
-                     slot + (4 * x + w) * 1024);
+        async_copy16_a(rows0 + (size_t)qq * D + ((pc ^ qswz32<D>(row)) & (KCH - 1)) * 8,
+                       slot + (4 * x + w) * 1024);
       }
     }
   };
   // row terms: chunk c = 8w + lane (lanes 0..7) of [z2 x64][D x64]
   const uint32_t roff = (uint32_t)(16 * (8 * w + (lane & 7)) + (w >= 2 ? 256 : 0));
-  auto copy_rowinfo = [&](int h, int i, char* slot) {
+  auto copy_rowinfo = [&](int h, int i, uint32_t slot) {
     const float* src = p.rowinfo + ((size_t)(b * p.heads_q + h) * p.tr + i) * kRowInfo;
-    if (lane < 8) async_copy16_so(src, roff, slot + 128 * w);
+    if (lane < 8) async_copy16_sa(src, roff, slot + 128 * w);
   };
 
   // transposing-read coordinates (as the forward's V^T operand): a lane
@@ -796,7 +797,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     auto issue_post = [&](int t) {
       const int it = c0 + (list[t] & 0xFFFFFFF);
       const int i = item_i(it), h = item_h(it);
-      char* slot = ring + (t % RP) * SP;
+      const uint32_t slot = ring_lds + (uint32_t)((t % RP) * SP);
       const size_t rows = (size_t)(b * p.heads_q + h) * p.nq * D;
       copy_tile(p.q + rows, i, slot);
       copy_tile(p.dout + rows, i, slot + TB);
@@ -1039,7 +1040,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
       const int s = s0 + lane;
       const int row = s / KCH, pc = s % KCH;
       const int kk = min(j * 64 + row, p.nk - 1);
-      async_copy16(base + (size_t)kk * D + ((pc ^ dqswz<D>(row)) & (KCH - 1)) * 8, slot + s0 * 8);
+      async_copy16_a(base + (size_t)kk * D + ((pc ^ dqswz<D>(row)) & (KCH - 1)) * 8,
+                     lds_addr(slot) + (uint32_t)s0 * 16u);
     }
   };
 

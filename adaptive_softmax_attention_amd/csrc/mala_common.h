@@ -105,58 +105,15 @@ __device__ __forceinline__ __bf16 to_bf16(float x) { return static_cast<__bf16>(
 // honour it as a clobber of inline assembly; the copies are safe because no
 // instruction the compiler generates in these kernels uses M0 (the generated
 // assembly is checked by tests/test_isa_checks.py).
-__device__ __forceinline__ void async_copy16(const void* gsrc, void* lds_base) {
-  // the LDS base is wave-uniform (M0); make that explicit to the compiler
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_base);
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off"
-      :
-      : "v"(gsrc), "s"(lds)
-      : "memory", "m0");
-}
-// 4-byte variant (one dword per lane, lane-contiguous at M0 + 4 * lane).
-__device__ __forceinline__ void async_copy4(const void* gsrc, void* lds_base) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_base);
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dword %0, off"
-      :
-      : "v"(gsrc), "s"(lds)
-      : "memory", "m0");
-}
-
-// Same copy with a wave-uniform 64-bit base (SGPR pair) and a 32-bit
-// per-lane byte offset: no per-lane 64-bit address arithmetic.
-__device__ __forceinline__ void async_copy16_so(const void* sbase, uint32_t voff, void* lds_base) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds_base);
-  // readfirstlane returns a signed int: go through uint32_t so that the low
-  // half is zero-extended (a sign-extended low half would corrupt the high
-  // half of the address)
-  const uint64_t a = (uint64_t)(uintptr_t)sbase;
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1"
-      :
-      : "v"(voff), "s"(sb), "s"(lds)
-      : "memory", "m0");
-}
 
 // LDS byte address of a __shared__ object (a 32-bit constant for the
 // compiler; no generic-pointer arithmetic or null checks).
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
 }
-// async_copy16_so with the LDS destination given as a byte address.
+// Copy with a wave-uniform 64-bit base (SGPR pair), a 32-bit per-lane byte
+// offset (no per-lane 64-bit address arithmetic) and the LDS destination as
+// a byte address (no generic-pointer conversion).
 __device__ __forceinline__ void async_copy16_sa(const void* sbase, uint32_t voff, uint32_t lds_byte) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_byte);
   const uint64_t a = (uint64_t)(uintptr_t)sbase;
@@ -169,6 +126,18 @@ __device__ __forceinline__ void async_copy16_sa(const void* sbase, uint32_t voff
       "global_load_lds_dwordx4 %0, %1"
       :
       : "v"(voff), "s"(sb), "s"(lds)
+      : "memory", "m0");
+}
+
+// Copy from a per-lane 64-bit address to an LDS byte address.
+__device__ __forceinline__ void async_copy16_a(const void* gsrc, uint32_t lds_byte) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_byte);
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(gsrc), "s"(lds)
       : "memory", "m0");
 }
 
