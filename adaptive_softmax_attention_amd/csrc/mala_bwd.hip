@@ -334,11 +334,14 @@ __global__ __launch_bounds__(576, 1) void bwd_score_kernel(BwdParams p) {
         const char* qt = ring + slot * SQ;
         const float* wr = (const float*)(qt + TB);
         const bool need_mask = diag_tile(p, i, jw) || (64 * jw + 64 > p.nk);
-        // the tile is kept as soon as one legal entry passes: the second
-        // 32-column half is scored only if the first has no passing entry
-        // (the dense path keeps every legal tile and scores nothing)
-        bool want = !kTest;
-        for (int qs = 0; qs < 2 && !want; ++qs) {
+        // Both 32-column halves are always scored, even when the first
+        // already has a passing entry (stopping early measured slower: the
+        // four waves that score an item then take different times, and its
+        // ring slot is refilled only after the last of them). The dense
+        // path keeps every legal tile and scores nothing.
+        bool hit = false;
+#pragma unroll
+        for (int qs = 0; qs < 2 && kTest; ++qs) {
           // B operands (Q^T: column 32 qs + l32) up front, then the products
           bf16x8 bq[NDC];
 #pragma unroll
@@ -382,8 +385,9 @@ __global__ __launch_bounds__(576, 1) void bwd_score_kernel(BwdParams p) {
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kt][e]);
-          want = wave_any(mx >= wr[32 * qs + l32]);
+          hit = hit || mx >= wr[32 * qs + l32];
         }
+        const bool want = kTest ? wave_any(hit) : true;
         kept += want ? 1 : 0;
         if (lane == 0) {
           const int bh = b * p.heads_q + kvh * p.group + ch;

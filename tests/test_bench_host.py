@@ -46,6 +46,8 @@ def test_source_hash_covers_the_kernels_and_not_the_host_api(tmp_path, monkeypat
     h0 = bench.kernel_source_hash()
     (csrc / "mala_api.hip").write_text("host c")
     assert bench.kernel_source_hash() == h0
+    (csrc / "mala_fwd.hip").write_text("kernel a // a note\n/* more\nnotes */\n\n")
+    assert bench.kernel_source_hash() == h0  # comments and blank lines change no kernel
     (csrc / "mala_fwd.hip").write_text("kernel a2")
     assert bench.kernel_source_hash() != h0
 
