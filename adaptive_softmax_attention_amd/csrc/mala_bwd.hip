@@ -1051,7 +1051,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
 
   // one kept tile: S^T, dP^T, dS^T, dQ^T += K^T dS^T, one half of the 64
   // keys (key subtiles 2kc, 2kc + 1) at a time
-  auto process = [&](const __bf16* kt, const __bf16* vt, int j) {
+  // (mid runs once, after the first half's S^T and dP^T products)
+  auto process = [&](const __bf16* kt, const __bf16* vt, int j, auto&& mid) {
     const bool need_mask = diag_tile(p, i, j) || (j * 64 + 64 > p.nk);
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
@@ -1091,6 +1092,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
               if (kk >= p.nk || (p.causal && kk > qq + p.off)) s[x][qs][r] = -INFINITY;
             }
       }
+      if (kc == 0) mid();
       // dS^T = P^T (dP^T - D) as B operands [key][query]: keys 32kc + 8g4 + e
       bf16x8 db[NQS];
 #pragma unroll
@@ -1168,13 +1170,26 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
     for (int t = 0; t < n; ++t) {
       vmcnt_wait_le(t + 1 < n ? 2 * CPT : 0);  // K, V of tile t + 1 may be in flight
       lds_barrier();
-      if (t + 2 < n) {
-        const int jn = list[t + 2] & 0xFFFFFF;
-        issue_tile(kbase, jn, k_ring[(t + 2) % RK]);
-        issue_tile(vbase, jn, v_ring[(t + 2) % RK]);
-      }
+      // K and V of tile t + 2 into the slots of tile t - 1 (done by every
+      // wave at the barrier). The two waves of a SIMD (w and w + 4) issue
+      // these copies at different points: waves 0-3 now, waves 4-7 after
+      // their first products when they process tile t, so that one wave's
+      // wait for the copy path overlaps the other's products.
+      auto issue_next = [&] {
+        if (t + 2 < n) {
+          const int jn = list[t + 2] & 0xFFFFFF;
+          issue_tile(kbase, jn, k_ring[(t + 2) % RK]);
+          issue_tile(vbase, jn, v_ring[(t + 2) % RK]);
+        }
+      };
       const int e = list[t];
-      if (valid && ((e >> (24 + blk)) & 1)) process(k_ring[t % RK], v_ring[t % RK], e & 0xFFFFFF);
+      const bool mine = valid && ((e >> (24 + blk)) & 1);
+      const bool late = w >= 4;
+      if (!late || !mine) issue_next();
+      if (mine)
+        process(k_ring[t % RK], v_ring[t % RK], e & 0xFFFFFF, [&] {
+          if (late) issue_next();
+        });
     }
   }
 
