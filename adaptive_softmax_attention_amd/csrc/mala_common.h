@@ -116,6 +116,9 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // a byte address (no generic-pointer conversion).
 __device__ __forceinline__ void async_copy16_sa(const void* sbase, uint32_t voff, uint32_t lds_byte) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_byte);
+  // readfirstlane returns a signed int: go through uint32_t so that the low
+  // half is zero-extended (a sign-extended low half would corrupt the high
+  // half of the address)
   const uint64_t a = (uint64_t)(uintptr_t)sbase;
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
