@@ -21,9 +21,17 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-I", INCLUDE, "-I", CSRC]
 
 
+# Per-file flags. The dK/dV pass (one wave per SIMD, bound by dependency
+# latency within the wave) is scheduled by LLVM's iterative ILP strategy,
+# which measured 2% faster on it and slower on the other passes.
+EXTRA = {"mala_bwd_kv.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    r = subprocess.run([HIPCC, *FLAGS, "-c", src, "-o", obj], capture_output=True, text=True)
+    extra = EXTRA.get(os.path.basename(src), [])
+    r = subprocess.run([HIPCC, *FLAGS, *extra, "-c", src, "-o", obj], capture_output=True,
+                       text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
     return obj

@@ -68,7 +68,8 @@ def test_host_schedule_model_uses_the_kernels_constants():
 
     import bwd_schedule as S
     csrc = os.path.join(ROOT, "adaptive_softmax_attention_amd", "csrc")
-    text = open(os.path.join(csrc, "mala_internal.h")).read() + open(os.path.join(csrc, "mala_bwd.hip")).read()
+    text = "".join(open(os.path.join(csrc, f)).read()
+                   for f in ("mala_internal.h", "mala_bwd.h", "mala_bwd.hip", "mala_bwd_kv.hip"))
 
     def const(name):
         m = re.search(r"constexpr int " + name + r"\s*=\s*(\d+)\s*;", text)

@@ -21,7 +21,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "adaptive_softmax_attention_amd", "csrc")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ("mala_fwd.hip", "mala_bwd.hip", "mala_decode.hip", "mala_api.hip")
+SOURCES = ("mala_fwd.hip", "mala_bwd.hip", "mala_bwd_kv.hip", "mala_decode.hip", "mala_api.hip")
 
 pytestmark = pytest.mark.skipif(not os.path.exists(HIPCC) and shutil.which("hipcc") is None,
                                 reason="hipcc not available")
