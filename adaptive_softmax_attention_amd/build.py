@@ -21,10 +21,12 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-I", INCLUDE, "-I", CSRC]
 
 
-# Per-file flags. The dK/dV pass (one wave per SIMD, bound by dependency
-# latency within the wave) is scheduled by LLVM's iterative ILP strategy,
-# which measured 2% faster on it and slower on the other passes.
-EXTRA = {"mala_bwd_kv.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
+# Per-file flags. The forward and the dK/dV pass are scheduled by LLVM's
+# iterative ILP strategy, which measured 1.7% (forward) and 3% (dK/dV)
+# faster; on the other backward passes it spills, and the decode does not
+# change.
+_ILP = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
+EXTRA = {"mala_fwd.hip": _ILP, "mala_bwd_kv.hip": _ILP}
 
 
 def _compile(src: str) -> str:
