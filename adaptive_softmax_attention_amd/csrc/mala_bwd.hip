@@ -241,6 +241,14 @@ __global__ __launch_bounds__(576, 1) void bwd_score_kernel(BwdParams p) {
     unsigned long long st_legal = 0, st_kept = 0, st_slots = 0;  // instrumentation
     // query block and group head of item k, advanced by two items per step
     int ci = p.tr - 1 - par / p.group, ch = par % p.group;
+    // the item's decision byte, stepped with (ci, ch) rather than recomputed:
+    // dmap[hoff + roff] with hoff = the map of head ch plus jw and roff = the
+    // tiles stored for the query blocks before ci (a causal row i holds
+    // i + cblk + 1 tiles below istar, tc from there on)
+    const long long ph = p.dmap_per_head;
+    const int istar = max(p.tc - p.cblk - 1, 0);
+    long long hoff = (long long)(b * p.heads_q + kvh * p.group + ch) * ph + jw;
+    long long roff = p.causal ? causal_row_start(ci, p.tc, p.cblk) : (long long)ci * p.tc;
     for (int k = par; k < n_items; k += 2) {
       const int slot = k % RQ;
       wait_for([&] {
@@ -309,7 +317,7 @@ __global__ __launch_bounds__(576, 1) void bwd_score_kernel(BwdParams p) {
         kept += want ? 1 : 0;
         if (lane == 0) {
           const int bh = b * p.heads_q + kvh * p.group + ch;
-          p.dmap[dmap_index(p, bh, i, jw)] = want ? 1 : 0;
+          p.dmap[hoff + roff] = want ? 1 : 0;
           if (kStats) {
             ++st_legal;
             if (want) {
@@ -325,9 +333,12 @@ __global__ __launch_bounds__(576, 1) void bwd_score_kernel(BwdParams p) {
       if (lane == 0)
         __hip_atomic_fetch_add(&done[slot], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
       ch += 2;
+      hoff += 2 * ph;
       while (ch >= p.group) {
         ch -= p.group;
+        hoff -= p.group * ph;
         --ci;
+        roff -= (p.causal && ci < istar) ? ci + p.cblk + 1 : p.tc;
       }
     }
     if (lane == 0) csum[w] = kept;
