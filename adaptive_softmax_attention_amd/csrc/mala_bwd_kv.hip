@@ -41,6 +41,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
 
   __shared__ __attribute__((aligned(16))) char ring[RP * SP];
   __shared__ int list[CH];
+  __shared__ int list_i[CH];  // query block of each listed item
   __shared__ int wcount[4];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -125,11 +126,12 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     toff[x] = (uint32_t)(row * D * 2 + ((pc ^ qswz32<D>(row)) & (KCH - 1)) * 16);
   }
   auto copy_tile = [&](const __bf16* rows0, int i, uint32_t slot) {
-    // rows0: row 0 of (b, h); block i lands swizzled in slot
+    // rows0: row 0 of (b, h); block i lands swizzled in the ring slot whose
+    // part for this wave starts at `slot` (the slot plus w KiB)
     if (64 * i + 64 <= p.nq) {
       const char* src = (const char*)(rows0 + (size_t)64 * i * D);
 #pragma unroll
-      for (int x = 0; x < CPW; ++x) async_copy16_sa(src, toff[x], slot + (4 * x + w) * 1024);
+      for (int x = 0; x < CPW; ++x) async_copy16_sa(src, toff[x], slot + x * 4096);
     } else {  // ragged last block: rows past the end re-read the last row
 #pragma unroll
       for (int x = 0; x < CPW; ++x) {
@@ -137,7 +139,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
         const int row = s / KCH, pc = s % KCH;
         const int qq = min(64 * i + row, p.nq - 1);
         async_copy16_a(rows0 + (size_t)qq * D + ((pc ^ qswz32<D>(row)) & (KCH - 1)) * 8,
-                       slot + (4 * x + w) * 1024);
+                       slot + x * 4096);
       }
     }
   };
@@ -171,15 +173,17 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
     const int nc = min(n_items - c0, CH);
 
     // ---- list of the chunk's items either block keeps (decision map
-    //      written by the scoring pass): entry = item | keep mask << 28 ----
+    //      written by the scoring pass): entry = item | keep mask << 28,
+    //      and the item's query block in list_i ----
     lds_barrier();  // the previous chunk's list and ring are no longer read
     int n_list = 0;
     for (int x0 = 0; x0 < nc; x0 += NT) {
       const int x = x0 + tid;
-      int mask = 0;
+      int mask = 0, i = 0;
       if (x < nc) {
         const int it = c0 + x;
-        const int i = item_i(it), h = item_h(it);
+        const int h = item_h(it);
+        i = item_i(it);
         const int bh = b * p.heads_q + h;
         if (legal(jA, i) && p.dmap[dmap_index(p, bh, i, jA)] != 0) mask |= 1;
         if (legal(jB, i) && p.dmap[dmap_index(p, bh, i, jB)] != 0) mask |= 2;
@@ -191,20 +195,27 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
       lds_barrier();
       int off = n_list;
       for (int y = 0; y < w; ++y) off += wcount[y];
-      if (mask) list[off + before] = x | (mask << 28);
+      if (mask) {
+        list[off + before] = x | (mask << 28);
+        list_i[off + before] = i;
+      }
       n_list += wcount[0] + wcount[1] + wcount[2] + wcount[3];
       lds_barrier();  // wcount reused; list entries visible
     }
     vmcnt_wait<0>();  // the map reads are done (the post phase counts copies only)
 
     // ======== post-score work of the listed items, three entries ahead ========
+    // (the item's query block comes from list_i, its head from
+    // it0 + it = (tr - 1 - i) group + (h - kvh group), without a division)
     auto issue_post = [&](int t) {
       const int it = c0 + (list[t] & 0xFFFFFFF);
-      const int i = item_i(it), h = item_h(it);
+      const int i = list_i[t];
+      const int h = kvh * p.group + (it0 + it) - (p.tr - 1 - i) * p.group;
       const uint32_t slot = ring_lds + (uint32_t)((t % RP) * SP);
       const size_t rows = (size_t)(b * p.heads_q + h) * p.nq * D;
-      copy_tile(p.q + rows, i, slot);
-      copy_tile(p.dout + rows, i, slot + TB);
+      const uint32_t wslot = slot + (uint32_t)w * 1024u;
+      copy_tile(p.q + rows, i, wslot);
+      copy_tile(p.dout + rows, i, wslot + TB);
       copy_rowinfo(h, i, slot + 2 * TB);
     };
     int issued = 0;
@@ -222,7 +233,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(BwdParams p) {
       }
       const int e = list[t];
       if (!((e >> (28 + sb)) & 1)) continue;
-      const int i = item_i(c0 + (e & 0xFFFFFFF));
+      const int i = list_i[t];
       const __bf16* qt = (const __bf16*)(ring + (t % RP) * SP);
       const __bf16* dt_ = qt + 64 * D;
       const float* ri = (const float*)(qt + 2 * 64 * D);
