@@ -658,6 +658,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
     }
   };
 
+  // K^T operands of the dQ product: the transposing read for key subtile
+  // pair kc, half hh and d chunk ds takes rows 32 kc + 4 hh + 8 g4 + l16 / 4
+  // at columns 16 ds + 4 (l16 % 4) .. + 3. The row swizzle depends only on
+  // 8 g4 + l16 / 4, so the lane's offset for chunk ds is fixed and (kc, hh)
+  // add a constant (an immediate of the read)
+  int ktr_off[NDS];
+#pragma unroll
+  for (int ds = 0; ds < NDS; ++ds) {
+    const int row = 8 * g4 + (l16 >> 2);
+    const int col = 16 * ds + 4 * (l16 & 3);
+    ktr_off[ds] = row * D + (((col >> 3) ^ dqswz<D>(row)) & (KCH - 1)) * 8 + (col & 7);
+  }
+
   // one kept tile: S^T, dP^T, dS^T, dQ^T += K^T dS^T, one half of the 64
   // keys (key subtiles 2kc, 2kc + 1) at a time
   // (mid runs once, after the first half's S^T and dP^T products)
@@ -718,12 +731,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
       for (int ds = 0; ds < NDS; ++ds) {
         short4v t2[2];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int row = 32 * kc + 8 * g4 + 4 * hh + (l16 >> 2);
-          const int col = 16 * ds + 4 * (l16 & 3);
-          t2[hh] =
-              lds_read_tr4(kt + row * D + (((col >> 3) ^ dqswz<D>(row)) & (KCH - 1)) * 8 + (col & 7));
-        }
+        for (int hh = 0; hh < 2; ++hh) t2[hh] = lds_read_tr4(kt + ktr_off[ds] + (32 * kc + 4 * hh) * D);
         const bf16x8 a = join_tr(t2[0], t2[1]);
 #pragma unroll
         for (int qs = 0; qs < NQS; ++qs) acc[ds][qs] = mfma16x16x32(a, db[qs], acc[ds][qs]);
@@ -776,6 +784,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
       issue_tile(kbase, jb, k_ring[1]);
       issue_tile(vbase, jb, v_ring[1]);
     }
+    // ring slots of tiles t and t + 2, stepped rather than taken modulo RK
+    // (the compiler turned t % RK into two running terms added at every
+    // operand read)
+    int cur = 0, ahead = 2 % RK;
     for (int t = 0; t < n; ++t) {
       vmcnt_wait_le(t + 1 < n ? 2 * CPT : 0);  // K, V of tile t + 1 may be in flight
       lds_barrier();
@@ -787,8 +799,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
       auto issue_next = [&] {
         if (t + 2 < n) {
           const int jn = list[t + 2] & 0xFFFFFF;
-          issue_tile(kbase, jn, k_ring[(t + 2) % RK]);
-          issue_tile(vbase, jn, v_ring[(t + 2) % RK]);
+          issue_tile(kbase, jn, k_ring[ahead]);
+          issue_tile(vbase, jn, v_ring[ahead]);
         }
       };
       const int e = list[t];
@@ -796,9 +808,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(BwdParams p) {
       const bool late = w >= 4;
       if (!late || !mine) issue_next();
       if (mine)
-        process(k_ring[t % RK], v_ring[t % RK], e & 0xFFFFFF, [&] {
+        process(k_ring[cur], v_ring[cur], e & 0xFFFFFF, [&] {
           if (late) issue_next();
         });
+      cur = cur + 1 == RK ? 0 : cur + 1;
+      ahead = ahead + 1 == RK ? 0 : ahead + 1;
     }
   }
 
